@@ -1,0 +1,371 @@
+"""ORACLE -- test infrastructure, not a product path.
+
+Plain, slow, obviously-correct CPU definitions of what the ZeRO owner-shard
+optimizer step computes.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no
+code with the HIP library (``zero_sharded_optimizer_owned_amd``) and imports
+nothing from it.
+
+Two halves:
+
+* pure Python (this file), following the pages in their own notation:
+  ``adam_step``, ``owner_ranges``, ``compare_owned_updates``, ``state_bytes``,
+  ``parameter_storage``, the flattened-buffer layout and the clip factor;
+* scalar C (``zero_oracle.c`` -> ``liboracle.so``) for the same arithmetic at
+  sizes Python loops cannot reach: fp32 rank reduce, accumulation, overflow
+  flag and squared norm, fp64 Adam/AdamW on fp32 state, fp16/bf16 encoders.
+
+Sources ("the pages"), cited by title and section:
+
+* [ZeRO-3 docs]  DeepSpeed ZeRO API documentation (zero3.rst): the list of
+  ZeRO stages and the JSON configuration examples (AdamW, fp16).
+* [ZeRO Q&A]     "How does DeepSpeed ZeRO stage 1, 2, and 3 partition optimizer
+  states, gradients, and parameters?": "Memory Footprint Reduction Matrix".
+* [Deep dive]    "Deep dive: DeepSpeed" (leetllm): sections "Count state before
+  choosing a stage", "Reduce first, then update the owned slice", "Let the
+  engine own the microstep", "Stage 3 needs a live working set", "Resume
+  training and export weights separately".
+
+Readings where the pages are silent are listed with each function.  Every
+function is pinned by the ``-m "not gpu"`` tests.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import math
+import os
+import subprocess
+from fractions import Fraction
+from typing import Dict, List, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F16, BF16, F32 = 1, 2, 3
+
+
+# ---------------------------------------------------------------------------
+# Pure-Python functions that follow the pages.
+# ---------------------------------------------------------------------------
+def adam_step(weight: float, first: float, second: float, gradient: float, step: int,
+              lr: float = 0.01, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8):
+    """One scalar Adam update in Python floats (fp64).
+
+    [Deep dive] "Reduce first, then update the owned slice": moments are
+    exponential averages of the gradient and of its square (uncentred), each
+    divided by ``1 - beta**step``; the step is ``lr * mhat / (sqrt(vhat) + eps)``
+    (eps outside the square root); steps count from 1.
+    """
+    first = beta1 * first + (1.0 - beta1) * gradient
+    second = beta2 * second + (1.0 - beta2) * gradient * gradient
+    mhat = first / (1.0 - beta1 ** step)
+    vhat = second / (1.0 - beta2 ** step)
+    return weight - lr * mhat / (math.sqrt(vhat) + eps), first, second
+
+
+def _positive_ints(*xs) -> bool:
+    return all(type(x) is int and x > 0 for x in xs)
+
+
+def owner_ranges(parameters: int, ranks: int) -> List[range]:
+    """Contiguous ownership: owner r holds ``[floor(P*r/R), floor(P*(r+1)/R))``.
+
+    [Deep dive] "Reduce first, then update the owned slice": owners are
+    contiguous and may be empty when there are more ranks than parameters.
+    """
+    return [range(parameters * r // ranks, parameters * (r + 1) // ranks) for r in range(ranks)]
+
+
+def pages_gradient(i: int, r: int, step: int) -> float:
+    """The lab's deterministic per-rank gradient for parameter i, rank r, step t."""
+    return ((i + 2 * r + step) % 7 - 3) / 10
+
+
+def compare_owned_updates(parameters: int, ranks: int, steps: int, grad=pages_gradient):
+    """Unsharded Adam on the rank-mean gradient vs owner-sharded Adam.
+
+    [Deep dive] "Reduce first, then update the owned slice": weights start at
+    ``0.1*i`` with zero moments; every step each rank contributes a gradient,
+    the unsharded run applies Adam to the mean over ranks; each owner reduces
+    only its own indices and applies Adam once to them.  Returns
+    ``(reference, reconstructed)``, lists of ``(w, m, v)`` per parameter.
+    """
+    if not _positive_ints(parameters, ranks, steps):
+        raise ValueError("parameters, ranks, and steps must be positive integers")
+    reference = [(0.1 * i, 0.0, 0.0) for i in range(parameters)]
+    owners = owner_ranges(parameters, ranks)
+    sharded = [{i: reference[i] for i in own} for own in owners]
+    for t in range(1, steps + 1):
+        local = [[grad(i, r, t) for i in range(parameters)] for r in range(ranks)]
+        mean = [sum(local[r][i] for r in range(ranks)) / ranks for i in range(parameters)]
+        reference = [adam_step(*reference[i], mean[i], t) for i in range(parameters)]
+        for r, own in enumerate(sharded):
+            reduced = {i: sum(row[i] for row in local) / ranks for i in own}
+            sharded[r] = {i: adam_step(*own[i], reduced[i], t) for i in own}
+    reconstructed = [state for own in sharded for state in own.values()]
+    return reference, reconstructed
+
+
+def state_bytes(parameters: int, ranks: int, param: int = 2, grad: int = 2,
+                optimizer: int = 12) -> Dict[str, Fraction]:
+    """Idealised per-rank persistent bytes for DP and ZeRO-1/2/3, as exact fractions.
+
+    [Deep dive] "Count state before choosing a stage" (and [ZeRO Q&A]
+    "Memory Footprint Reduction Matrix"): DP replicates everything; ZeRO-1
+    shards the optimizer state; ZeRO-2 also the gradients; ZeRO-3 also the
+    parameters.  Inputs must be positive integers.
+    """
+    if not _positive_ints(parameters, ranks, param, grad, optimizer):
+        raise ValueError("counts and byte widths must be positive integers")
+    shard = Fraction(parameters, ranks)
+    return {
+        "DP": Fraction(parameters * (param + grad + optimizer)),
+        "ZeRO-1": parameters * (param + grad) + shard * optimizer,
+        "ZeRO-2": parameters * param + shard * (grad + optimizer),
+        "ZeRO-3": shard * (param + grad + optimizer),
+    }
+
+
+def parameter_storage(layer_sizes: Sequence[int], ranks: int, live_layers: Sequence[int]):
+    """ZeRO-3 parameter elements: resident shards + separate full gather buffers.
+
+    [Deep dive] "Stage 3 needs a live working set": each tensor's shard is
+    ``ceil(n/R)`` elements; a live (gathered) tensor adds a separate padded
+    buffer of ``R * ceil(n/R)`` elements.  Returns ``(resident, gathered, total)``.
+    """
+    if type(ranks) is not int or ranks <= 0:
+        raise ValueError("ranks must be a positive integer")
+    if not layer_sizes or any(type(n) is not int or n <= 0 for n in layer_sizes):
+        raise ValueError("tensor sizes must be positive integers")
+    if any(type(i) is not int or not 0 <= i < len(layer_sizes) for i in live_layers) or \
+            len(set(live_layers)) != len(live_layers):
+        raise ValueError("live tensor indices must be distinct and in range")
+    shards = [-(-n // ranks) for n in layer_sizes]
+    resident = sum(shards)
+    gathered = sum(shards[i] * ranks for i in live_layers)
+    return resident, gathered, resident + gathered
+
+
+# ---------------------------------------------------------------------------
+# Flattened, padded parameter buffer (reading: the pages leave padding open).
+# ---------------------------------------------------------------------------
+def layout(numels: Sequence[int], ranks: int, align: int):
+    """Tensor offsets, padded total and owner ranges of the flat buffer.
+
+    Reading of the pages (which apply the floor ownership formula to an
+    unpadded count and say the lab does not simulate padding): every tensor,
+    the last included, is padded up to a multiple of ``align`` elements;
+    tensor k starts at the sum of the padded sizes before it; ownership is the
+    floor formula applied to the padded total.  Returns
+    ``(offsets, padded_total, [(begin, end) per owner])``.
+    """
+    if ranks <= 0 or align <= 0 or not numels or any(n <= 0 for n in numels):
+        raise ValueError("sizes, ranks and alignment must be positive")
+    offsets, total = [], 0
+    for n in numels:
+        offsets.append(total)
+        total += -(-n // align) * align
+    owners = [(r.start, r.stop) for r in owner_ranges(total, ranks)] if total else []
+    return offsets, total, owners
+
+
+def real_ranges(numels: Sequence[int], offsets: Sequence[int], begin: int, end: int):
+    """The owner's real (non-padding) elements: ``[off_k, off_k+n_k) ∩ [begin, end)``."""
+    out = []
+    for n, off in zip(numels, offsets):
+        b, e = max(begin, off), min(end, off + n)
+        if b < e:
+            out.append((b, e))
+    return out
+
+
+def clip_coef(sumsq: float, max_norm: float = 1.0, eps: float = 1e-6) -> float:
+    """Global-norm clip factor ``min(1, max_norm / (sqrt(sumsq) + eps))``.
+
+    Reading: the pages name no clipping rule; this is the common
+    ``clip_grad_norm_`` convention (eps 1e-6, clamp at 1).
+    """
+    return min(1.0, max_norm / (math.sqrt(sumsq) + eps))
+
+
+# ---------------------------------------------------------------------------
+# Scalar C half.
+# ---------------------------------------------------------------------------
+class Hyper(ct.Structure):
+    _fields_ = [("lr", ct.c_double), ("beta1", ct.c_double), ("beta2", ct.c_double),
+                ("eps", ct.c_double), ("weight_decay", ct.c_double), ("adamw", ct.c_int32),
+                ("step", ct.c_uint64), ("clip_coef", ct.c_double)]
+
+
+def hyper(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, adamw=True, step=1,
+          clip_coef=1.0) -> Hyper:
+    if step < 1:
+        raise ValueError("Adam steps count from 1")
+    return Hyper(lr, beta1, beta2, eps, weight_decay, 1 if adamw else 0, step, clip_coef)
+
+
+def build() -> str:
+    """Compile zero_oracle.c with gcc into liboracle.so (no fast-math, no FMA contraction)."""
+    src = os.path.join(_HERE, "zero_oracle.c")
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
+           "-shared", "-Wall", src, "-o", tmp, "-lm"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("building the oracle failed:\n" + res.stderr)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ct.CDLL(LIB_PATH)
+        P, U64, F, D, I = ct.c_void_p, ct.c_uint64, ct.c_float, ct.c_double, ct.c_int
+        L.oracle_f32_to_f16.restype = ct.c_uint16
+        L.oracle_f32_to_f16.argtypes = [F]
+        L.oracle_f32_to_bf16.restype = ct.c_uint16
+        L.oracle_f32_to_bf16.argtypes = [F]
+        L.oracle_f16_value.restype = D
+        L.oracle_f16_value.argtypes = [ct.c_uint16]
+        L.oracle_bf16_value.restype = D
+        L.oracle_bf16_value.argtypes = [ct.c_uint16]
+        L.oracle_encode16.argtypes = [P, U64, I, P]
+        L.oracle_reduce.argtypes = [ct.c_uint32, I, P, U64, F, I, P]
+        L.oracle_accumulate.argtypes = [I, P, U64, I, P]
+        L.oracle_grad_check.argtypes = [P, U64, P, P]
+        L.oracle_clip_coef.restype = D
+        L.oracle_clip_coef.argtypes = [D, D, D]
+        L.oracle_adam_f64.argtypes = [U64, P, P, P, P, ct.POINTER(Hyper)]
+        L.oracle_adam_f32.argtypes = [U64, P, P, P, P, ct.POINTER(Hyper)]
+        L.oracle_owner_step.argtypes = [ct.c_uint32, I, P, U64, P, F, U64, P, P, P, P, P, U64, P,
+                                        I, U64, ct.POINTER(Hyper)]
+        L.oracle_num_threads.restype = I
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return ct.c_void_p(a.ctypes.data)
+
+
+def _storage(a: np.ndarray, dtype: int) -> np.ndarray:
+    want = np.float32 if dtype == F32 else np.uint16
+    if a.dtype != want or not a.flags["C_CONTIGUOUS"]:
+        raise TypeError(f"expected contiguous {want.__name__} storage for dtype {dtype}")
+    return a
+
+
+def _ptr_array(bufs: Sequence[np.ndarray]):
+    arr = (ct.c_void_p * max(1, len(bufs)))()
+    for r, b in enumerate(bufs):
+        arr[r] = b.ctypes.data
+    return arr
+
+
+def encode16(x: np.ndarray, dtype: int) -> np.ndarray:
+    """Round fp32 values to fp16/bf16 bit patterns (nearest, ties to even)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().oracle_encode16(_ptr(x), x.size, dtype, _ptr(out))
+    return out
+
+
+def decode16(bits: np.ndarray, dtype: int) -> np.ndarray:
+    """Exact fp64 values of fp16/bf16 bit patterns."""
+    f = lib().oracle_f16_value if dtype == F16 else lib().oracle_bf16_value
+    return np.array([f(int(b)) for b in np.asarray(bits).ravel()], dtype=np.float64).reshape(
+        np.shape(bits))
+
+
+def reduce(grads: Sequence[np.ndarray], dtype: int, divisor: float, out: np.ndarray = None,
+           accumulate: bool = False) -> np.ndarray:
+    """fp32 rank reduce: ``(start + g_0 + ... + g_{R-1}) / divisor`` in rank order."""
+    n = grads[0].size
+    for g in grads:
+        _storage(g, dtype)
+        if g.size != n:
+            raise ValueError("rank buffers differ in length")
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing output")
+        out = np.empty(n, dtype=np.float32)
+    lib().oracle_reduce(len(grads), dtype, _ptr_array(grads), n, divisor, int(accumulate),
+                        _ptr(out))
+    return out
+
+
+def accumulate(g: np.ndarray, dtype: int, acc: np.ndarray, first: bool) -> np.ndarray:
+    _storage(g, dtype)
+    lib().oracle_accumulate(dtype, _ptr(g), g.size, int(first), _ptr(acc))
+    return acc
+
+
+def grad_check(g: np.ndarray) -> Tuple[int, float]:
+    """(overflow flag, squared norm in fp64) of an fp32 gradient."""
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    flag = np.zeros(1, dtype=np.int32)
+    s = np.zeros(1, dtype=np.float64)
+    lib().oracle_grad_check(_ptr(g), g.size, _ptr(flag), _ptr(s))
+    return int(flag[0]), float(s[0])
+
+
+def adam_f64(g, w, m, v, h: Hyper):
+    """fp64 state update in place (the pages' arithmetic, vectorised over elements)."""
+    for a in (g, w, m, v):
+        if a.dtype != np.float64 or not a.flags["C_CONTIGUOUS"]:
+            raise TypeError("adam_f64 needs contiguous float64 arrays")
+    lib().oracle_adam_f64(g.size, _ptr(g), _ptr(w), _ptr(m), _ptr(v), ct.byref(h))
+
+
+def adam_f32(g, w, m, v, h: Hyper):
+    """fp32 stored state, fp64 arithmetic, rounded once on store; in place."""
+    for a in (g, w, m, v):
+        if a.dtype != np.float32 or not a.flags["C_CONTIGUOUS"]:
+            raise TypeError("adam_f32 needs contiguous float32 arrays")
+    lib().oracle_adam_f32(g.size, _ptr(g), _ptr(w), _ptr(m), _ptr(v), ct.byref(h))
+
+
+def owner_step(ranges: Sequence[Tuple[int, int]], h: Hyper, w: np.ndarray, m: np.ndarray,
+               v: np.ndarray, local_base: int, *, grads: Sequence[np.ndarray] = (),
+               gdtype: int = F32, grad_base: int = 0, divisor: float = 1.0,
+               reduced_g: np.ndarray = None, p16: np.ndarray = None, pdtype: int = 0,
+               param_base: int = 0) -> None:
+    """The owner step over its real elements, in place.
+
+    Flat index f reads ``grads[r][f - grad_base]`` (or ``reduced_g[f - local_base]``),
+    updates ``w/m/v[f - local_base]`` and writes ``p16[f - param_base]``.
+    """
+    for a in (w, m, v):
+        _storage(a, F32)
+    for g in grads:
+        _storage(g, gdtype)
+    rb = np.array([b for b, _ in ranges], dtype=np.uint64)
+    re_ = np.array([e for _, e in ranges], dtype=np.uint64)
+    for b, e in ranges:
+        if b < local_base or e - local_base > w.size:
+            raise IndexError("range outside the owner-local arrays")
+        if reduced_g is None and (b < grad_base or any(e - grad_base > g.size for g in grads)):
+            raise IndexError("range outside the rank buffers")
+        if p16 is not None and pdtype and (b < param_base or e - param_base > p16.size):
+            raise IndexError("range outside the 16-bit buffer")
+    if reduced_g is not None:
+        _storage(reduced_g, F32)
+    lib().oracle_owner_step(
+        len(grads), gdtype, _ptr_array(grads), grad_base,
+        _ptr(reduced_g) if reduced_g is not None else None, divisor, len(ranges),
+        _ptr(rb) if len(ranges) else None, _ptr(re_) if len(ranges) else None,
+        _ptr(w), _ptr(m), _ptr(v), local_base,
+        _ptr(p16) if p16 is not None else None, pdtype if p16 is not None else 0, param_base,
+        ct.byref(h))
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
