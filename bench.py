@@ -1,0 +1,392 @@
+"""Benchmark of the ZeRO owner-shard optimizer step on one MI355X.
+
+One step = one pass of the owner's whole hot path over one batch of synthetic
+input (inputs resident in HBM before the timed region):
+  --config 2 (default): 1.5e9-parameter flat buffer, R=4, owner 1 (3.75e8
+      parameters): fused fp16 rank reduce + AdamW + fp16 write-back, one launch.
+  --config 3: Llama-style 289-tensor list (6,607,339,520 parameters), 64-element
+      alignment, R=8, owner 1: fused bf16 reduce + AdamW + bf16 write-back.
+  --config 4: 7e10 flat, R=64, owner 1 (1.09375e9): fp16 grads scaled by 2^16;
+      reduce + overflow/norm check, host skip/clip decision, AdamW from the
+      stored fp32 gradient; inf/NaN injected in one step of every four.
+  --config 5: 10,000 log-uniform tensors (~2e9), R=16: eight bf16 microstep
+      accumulations into the local fp32 buffer, then the owner's fused
+      fp32-rank reduce + AdamW + bf16 write-back.
+
+Prints one JSON line: owned parameters updated per second, achieved HBM GB/s of
+the dominant kernel against the 8 TB/s peak, and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "owned-shard params updated/sec + achieved HBM GB/s (fraction of MI355X peak)"
+PEAK_GBPS = 8000.0
+HP = dict(lr=1e-3, beta1=0.8, beta2=0.999, eps=1e-8, weight_decay=3e-7, adamw=True)
+FIRST_STEP = 11  # the state stands for an optimizer after ten warm-up updates
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4, 5))
+    ap.add_argument("--grid", type=int, default=0, help="persistent grid blocks (0: library default)")
+    ap.add_argument("--chunk", type=int, default=16384, help="max chunk elements")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    p = os.path.join(ROOT, "zero_sharded_optimizer_owned_amd", "csrc", "device.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_record(name: str):
+    """Counter-derived HBM bytes per launch, if taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------- workloads
+def llama_numels():
+    d, ff, vocab = 4096, 11008, 32000
+    layer = [d * d] * 4 + [d * ff, d * ff, ff * d, d, d]
+    return [vocab * d] + layer * 32
+
+
+def config5_numels(seed=5):
+    import numpy as np
+
+    import synth
+
+    s = synth.log_uniform_sizes(seed, 10_000, 64, 1 << 24).astype(np.float64)
+    s[0] = 1 << 24          # one tensor at the top of the range
+    s[1:11] = 64            # at least ten at the bottom
+    rest = s[11:]
+    scale = (2e9 - (1 << 24) - 640) / rest.sum()
+    s[11:] = np.maximum(64, np.floor(rest * scale))
+    return [int(x) for x in s]
+
+
+def fill(t, seed, stream, rank, index0, dist, scale, step=0):
+    import synth
+
+    synth.device_fill(t, synth.stream_key(seed, stream, rank, step), index0, dist, scale)
+
+
+class Workload:
+    """Device buffers and the step function of one configuration."""
+
+    def __init__(self, cfg: int, chunk: int, grid: int):
+        import torch
+
+        import synth
+        import zero_sharded_optimizer_owned_amd as zs
+
+        self.cfg, self.grid = cfg, grid
+        dev = torch.device("cuda")
+        self.dev = dev
+        owner = 1
+        if cfg == 2:
+            numels, R, A, gdt, pdt = [1_500_000_000], 4, 64, torch.float16, torch.float16
+            self.name = "flat 1.5e9 params, R=4, owner 1 of 4 (3.75e8), fp16 grads, fp16 write-back"
+        elif cfg == 3:
+            numels, R, A, gdt, pdt = llama_numels(), 8, 64, torch.bfloat16, torch.bfloat16
+            self.name = ("Llama-style 289 tensors (6,607,339,520 params), 64-elem alignment, R=8, owner 1 "
+                         "of 8, bf16 grads, bf16 write-back")
+        elif cfg == 4:
+            numels, R, A, gdt, pdt = [70_000_000_000], 64, 64, torch.float16, torch.float16
+            self.name = ("flat 7e10 params, R=64, owner 1 of 64 (1.09375e9), fp16 grads x 2^16, overflow skip, "
+                         "clip 1.0, fp16 write-back")
+        else:
+            numels, R, A, gdt, pdt = config5_numels(), 16, 64, torch.float32, torch.bfloat16
+            self.name = ("10,000 log-uniform tensors (~2e9 params), R=16, owner 1 of 16, 8 bf16 microsteps "
+                         "into fp32, bf16 write-back")
+        self.numels, self.R = numels, R
+        self.sh = zs.OwnerShard(numels, R, owner, align=A, max_chunk=chunk, device=dev)
+        sh = self.sh
+        lb, end = sh.local_base, sh.end
+        seed = cfg
+        # owner-local rank slices (what a reduce-scatter would deliver), flat-indexed from lb
+        self.grads = []
+        self.grad_scale = 65536.0 * 1e-3 if cfg == 4 else 1e-3
+        if cfg != 5:
+            for r in range(R):
+                t = torch.empty(end - lb, dtype=gdt, device=dev)
+                fill(t, seed, synth.STREAM_GRAD, r, lb, synth.DIST_NORMAL, self.grad_scale)
+                self.grads.append(t)
+        sh.alloc_state()
+        fill(sh.master, seed, synth.STREAM_MASTER, 0, lb, synth.DIST_NORMAL, 0.02)
+        fill(sh.exp_avg, seed, synth.STREAM_EXP_AVG, 0, lb, synth.DIST_NORMAL, 5e-4)
+        fill(sh.exp_avg_sq, seed, synth.STREAM_EXP_AVG_SQ, 0, lb, synth.DIST_SQUARE, 1e-4)
+        # 16-bit compute copy: the full flat buffer (ZeRO-1/2) except for the 70e9 case,
+        # where only the owner's slice is held (ZeRO-3 style), param_base = lb
+        if cfg == 4:
+            self.p16, self.param_base = torch.zeros(end - lb, dtype=pdt, device=dev), lb
+            self.g32 = torch.empty(end - lb, dtype=torch.float32, device=dev)
+            self.ov = torch.zeros(1, dtype=torch.int32, device=dev)
+            self.ss = torch.zeros(1, dtype=torch.float64, device=dev)
+            self.ws = zs.check_workspace(dev)
+            self.divisor = float(R) * 65536.0
+        else:
+            self.p16 = torch.zeros(sh.padded_total, dtype=pdt, device=dev)
+            self.param_base = 0
+            self.divisor = float(R)
+        if cfg == 5:
+            self._setup_microsteps(seed)
+        self.t = FIRST_STEP
+        self.skipped = 0
+        self.kernel_bytes = self.algorithmic_bytes()
+        torch.cuda.synchronize()
+
+    def _setup_microsteps(self, seed):
+        import torch
+
+        import synth
+        import zero_sharded_optimizer_owned_amd as zs
+
+        sh = self.sh
+        n = sh.padded_total
+        # local rank's eight bf16 microstep gradients over the whole flat buffer
+        self.micro = []
+        for k in range(8):
+            t = torch.empty(n, dtype=torch.bfloat16, device=self.dev)
+            fill(t, seed, synth.STREAM_MICRO, self.sh.owner, 0, synth.DIST_NORMAL, 1e-3, step=k)
+            self.micro.append(t)
+        self.acc = torch.empty(n, dtype=torch.float32, device=self.dev)
+        # the other ranks' accumulated gradients for this owner's slice: each is the
+        # same eight-microstep accumulation of that rank's own microstep gradients
+        lb, end = sh.local_base, sh.end
+        tmp = torch.empty(end - lb, dtype=torch.bfloat16, device=self.dev)
+        for r in range(self.R):
+            if r == sh.owner:
+                self.grads.append(None)
+                continue
+            acc_r = torch.empty(end - lb, dtype=torch.float32, device=self.dev)
+            for k in range(8):
+                fill(tmp, seed, synth.STREAM_MICRO, r, lb, synth.DIST_NORMAL, 1e-3, step=k)
+                zs.zero_reduce_owned([tmp], lb, end - lb, 1.0, acc_r, grad_base=lb, out_base=lb,
+                                     accumulate=k > 0)
+            self.grads.append(acc_r)
+        # the owner's own slice is a view of its accumulation buffer
+        self.grads[sh.owner] = self.acc[lb:end]
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes the dominant kernel must move per launch."""
+        n = self.sh.n_real
+        if self.cfg == 4:
+            return n * 30  # adam from the stored gradient: g 4 + w,m,v 12 + 12 + p16 2
+        gw = self.grads[0].element_size() if self.grads[0] is not None else 4
+        return n * (self.R * gw + 24 + self.p16.element_size())
+
+    def step_bytes(self, overflow: bool) -> int:
+        n = self.sh.n_real
+        if self.cfg == 4:
+            return n * (self.R * 2 + 4) + (0 if overflow else n * 30)
+        if self.cfg == 5:
+            P = self.sh.padded_total
+            return P * (6 + 7 * 10) + self.kernel_bytes
+        return self.kernel_bytes
+
+    # one full step of the owner's hot path
+    def step(self, timing=None):
+        import torch
+
+        import zero_sharded_optimizer_owned_amd as zs
+
+        sh = self.sh
+        if self.cfg == 5:
+            for k, g in enumerate(self.micro):
+                zs.zero_reduce_owned([g], 0, sh.padded_total, 1.0, self.acc, accumulate=k > 0)
+        if self.cfg == 4:
+            inject = (self.t - FIRST_STEP) % 4 == 3
+            if inject:  # +inf in one rank, NaN in another (input preparation, two stores)
+                self.grads[5][12345] = float("inf")
+                self.grads[17][777_777] = float("nan")
+            zs.zero_reduce_owned(self.grads, sh.begin, sh.end - sh.begin, self.divisor, self.g32,
+                                 grad_base=sh.local_base, out_base=sh.local_base,
+                                 check=(self.ov, self.ss, self.ws))
+            flag, sumsq = int(self.ov.item()), float(self.ss.item())  # 12 bytes to the host
+            if inject:
+                self.grads[5][12345] = 0.0
+                self.grads[17][777_777] = 0.0
+            if flag:
+                self.skipped += 1
+                return True
+            coef = zs.zero_clip_coef(sumsq, 1.0, 1e-6)
+            if timing is not None:
+                timing[0].record()
+            sh.adam_step(step=self.t, hyper=HP, reduced_g=self.g32, param16=self.p16,
+                         param_base=self.param_base, clip_coef=coef, grid_blocks=self.grid)
+            if timing is not None:
+                timing[1].record()
+            self.t += 1
+            return False
+        if timing is not None:
+            timing[0].record()
+        sh.adam_step(step=self.t, hyper=HP, rank_grads=self.grads, grad_base=sh.local_base,
+                     divisor=self.divisor, param16=self.p16, param_base=self.param_base,
+                     grid_blocks=self.grid)
+        if timing is not None:
+            timing[1].record()
+        self.t += 1
+        return False
+
+
+# ---------------------------------------------------------------- CPU oracle leg
+def cpu_baseline(w: Workload, seconds: float):
+    """The oracle on a bounded prefix of the same owner's work, on the host cores."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    sh = w.sh
+    cfg = w.cfg
+    # real elements in the sample: sized so that generating its inputs stays a few seconds
+    budget = {2: 1 << 24, 3: 1 << 23, 4: 1 << 21, 5: 1 << 20}[cfg]
+    ranges, left = [], budget
+    for c in sh.chunks:
+        if left <= 0:
+            break
+        take = min(int(c["len"]), left)
+        ranges.append((int(c["flat"]), int(c["flat"]) + take))
+        left -= take
+    lo, hi = ranges[0][0], ranges[-1][1]
+    lb = lo & ~7
+    seed = cfg
+    idx = synth.arange(lb, hi)
+    gcode = {2: synth.F16, 3: synth.BF16, 4: synth.F16, 5: synth.F32}[cfg]
+    scale = w.grad_scale if cfg != 5 else 1e-3
+    if cfg == 5:
+        grads = []
+        for r in range(w.R):
+            acc = np.zeros(hi - lb, dtype=np.float32)
+            for k in range(8):
+                g = synth.values(synth.stream_key(seed, synth.STREAM_MICRO, r, k), idx, synth.DIST_NORMAL,
+                                 1e-3, synth.BF16)
+                oracle.accumulate(g, synth.BF16, acc, first=(k == 0))
+            grads.append(acc)
+    else:
+        grads = [synth.values(synth.stream_key(seed, synth.STREAM_GRAD, r), idx, synth.DIST_NORMAL,
+                              scale, gcode) for r in range(w.R)]
+    mk = lambda st, dist, s: synth.values_f32(synth.stream_key(seed, st, 0), idx, dist, s)
+    w0 = mk(synth.STREAM_MASTER, synth.DIST_NORMAL, 0.02)
+    m0 = mk(synth.STREAM_EXP_AVG, synth.DIST_NORMAL, 5e-4)
+    v0 = mk(synth.STREAM_EXP_AVG_SQ, synth.DIST_SQUARE, 1e-4)
+    pcode = synth.F16 if cfg in (2, 4) else synth.BF16
+    p16 = np.zeros(hi - lb, dtype=np.uint16)
+    n_real = sum(e - b for b, e in ranges)
+    done, el, reps = 0, 0.0, 0
+    while True:
+        wc, mc, vc = w0.copy(), m0.copy(), v0.copy()
+        t_start = time.perf_counter()
+        if cfg == 4:
+            g = oracle.reduce([x[lo - lb:hi - lb] for x in grads], gcode, w.divisor)
+            flag, sumsq = oracle.grad_check(g)
+            gfull = np.zeros(hi - lb, dtype=np.float32)
+            gfull[lo - lb:] = g
+            oracle.owner_step(ranges, oracle.hyper(step=FIRST_STEP, clip_coef=oracle.clip_coef(sumsq), **HP),
+                              wc, mc, vc, lb, reduced_g=gfull, p16=p16, pdtype=pcode, param_base=lb)
+        else:
+            oracle.owner_step(ranges, oracle.hyper(step=FIRST_STEP, **HP), wc, mc, vc, lb, grads=grads,
+                              gdtype=gcode, grad_base=lb, divisor=w.divisor, p16=p16, pdtype=pcode,
+                              param_base=lb)
+        el += time.perf_counter() - t_start
+        done += n_real
+        reps += 1
+        if el >= seconds or reps >= 1000:
+            break
+    return {"value": done / el, "unit": "params/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {n_real} real elements of the owner's shard, {reps} oracle step(s) "
+                      f"({'reduce+check+clip+AdamW' if cfg == 4 else 'reduce+AdamW+cast'}; "
+                      f"{'microstep accumulation untimed; ' if cfg == 5 else ''}inputs pre-generated)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU exchange "
+              "around the owner step is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import zero_sharded_optimizer_owned_amd as zs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    zs.lib()
+    w = Workload(args.config, args.chunk, args.grid)
+    for _ in range(args.warmup):
+        w.step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    overflow_steps = 0
+    w.skipped = 0
+    torch.cuda.synchronize()
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_all0.record()
+    launched = []
+    for i in range(args.steps):
+        skipped = w.step(timing=(starts[i], ends[i]))
+        launched.append(not skipped)
+        overflow_steps += int(skipped)
+    t_all1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_all0.elapsed_time(t_all1)
+    ms_step = total_ms / args.steps
+    kms = [s.elapsed_time(e) for s, e, ok in zip(starts, ends, launched) if ok]
+    kernel_ms = sum(kms) / len(kms)
+    n = w.sh.n_real
+    updated = n * (args.steps - overflow_steps)
+    value = updated / (total_ms / 1e3)
+    step_bytes = sum(w.step_bytes(not ok) for ok in launched)
+    gbps_step = step_bytes / (total_ms / 1e3) / 1e9
+    achieved = w.kernel_bytes / (kernel_ms / 1e3) / 1e9
+    kname = "adam_step_" + {2: "f16_f16", 3: "bf16_bf16", 4: "reduced_f16", 5: "f32_bf16"}[args.config]
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic_record(f"{kname}_config{args.config}"),
+                "kernel": kname, "kernel_ms": round(kernel_ms, 4),
+                "bytes_per_launch": w.kernel_bytes}
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "params/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "config": args.config, "owned_params": n,
+                   "ranks": w.R, "padded_total": w.sh.padded_total, "chunks": int(w.sh.chunks.size),
+                   "parallelism": "1 GPU (owner shard; no collectives)"},
+        "gbps": round(gbps_step, 1), "frac_of_peak": round(gbps_step / PEAK_GBPS, 4),
+        "overflow_steps": overflow_steps, "wall_s": round(wall, 3),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

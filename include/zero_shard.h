@@ -1,0 +1,262 @@
+/*
+ * zero_shard.h -- C ABI of libzero_shard.so: the ZeRO owner-shard optimizer
+ * step on one MI355X (gfx950).
+ *
+ * In ZeRO stages 1-3 each data-parallel rank owns one contiguous slice of the
+ * flattened parameter buffer and keeps the fp32 master weights and Adam
+ * moments for that slice only.  At an optimizer boundary the owner reduces
+ * the ranks' gradients for its slice (equally weighted mean), applies
+ * Adam/AdamW once to the reduced gradient and writes the 16-bit compute copy
+ * of its updated weights.  This library performs that step inside one GPU's
+ * memory: the R ranks' gradients for the owned slice are R device buffers.
+ *
+ * Sources, cited by page title and section:
+ *   [ZeRO-3 docs]  DeepSpeed ZeRO API documentation (zero3.rst): the stage
+ *                  list; the JSON examples (AdamW, fp16).
+ *   [ZeRO Q&A]     "How does DeepSpeed ZeRO stage 1, 2, and 3 partition
+ *                  optimizer states, gradients, and parameters?":
+ *                  "Memory Footprint Reduction Matrix".
+ *   [Deep dive]    "Deep dive: DeepSpeed" (leetllm): "Count state before
+ *                  choosing a stage", "Reduce first, then update the owned
+ *                  slice", "Let the engine own the microstep".
+ *
+ * Conventions for every call:
+ *   - Return 0 (ZERO_OK) or a negative ZERO_E* code; zero_last_error() then
+ *     gives a message (thread-local, valid until the next call on the thread).
+ *     No exceptions escape, nothing exits the process.
+ *   - The caller owns every buffer.  The library allocates no memory and
+ *     keeps no state between calls (apart from a per-device cache of the
+ *     compute-unit count).  Arguments are validated before anything is
+ *     launched; a call that fails validation launches nothing and writes
+ *     nothing.  Buffer extents cannot be seen through plain pointers: the
+ *     caller guarantees the sizes stated for each argument.
+ *   - Device calls are asynchronous on `stream`; errors of the running
+ *     kernels surface at the caller's next synchronisation of the stream.
+ *   - Device pointers must be 16-byte aligned.  Flat index f of a buffer with
+ *     base index B lives at element f - B; every base index is a multiple
+ *     of 8 so that 128-bit vectors of all streams start at the same flat
+ *     indices.
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum zero_status {
+  ZERO_OK = 0,
+  ZERO_EINVAL = -1, /* bad argument: nothing launched, nothing written */
+  ZERO_ERANGE = -2, /* output capacity too small, or an integer result above 2^64 - 1 */
+  ZERO_EHIP = -3    /* HIP runtime or launch error */
+};
+
+enum zero_dtype {
+  ZERO_NONE = 0, /* no 16-bit write-back (fp32 model) */
+  ZERO_F16 = 1,  /* IEEE binary16 */
+  ZERO_BF16 = 2, /* bfloat16 */
+  ZERO_F32 = 3   /* IEEE binary32 */
+};
+
+/* Most rank buffers one reduce can read (pointers travel as kernel arguments). */
+#define ZERO_MAX_RANKS 256
+/* Workspace bytes the squared-norm / overflow reduction needs (per-block partials). */
+#define ZERO_CHECK_WS_BYTES 65536
+
+/* Message for the last failed call on this thread ("" if none). */
+const char *zero_last_error(void);
+
+/* ----------------------------------------------------------------------------
+ * zero_shard_layout -- flattened, padded buffer and contiguous ownership.
+ *
+ * [Deep dive] "Reduce first, then update the owned slice": owner r of R holds
+ * the contiguous range [floor(P*r/R), floor(P*(r+1)/R)); owners may be empty
+ * when R exceeds P.  The pages do not give the padding; here every tensor,
+ * the last included, is padded up to a multiple of `align_elems` elements
+ * (tensor k starts at the sum of the padded sizes before it) and ownership is
+ * taken over the padded total P.  Padding is owned but never read or written
+ * by the device calls.
+ *
+ * numel[n_tensors]          in : element count of each tensor, all > 0
+ * ranks, align_elems        in : R >= 1, alignment in elements >= 1
+ * tensor_offset[n_tensors]  out: flat index of each tensor's first element
+ * padded_total              out: P
+ * owner_begin/end[ranks]    out: owner ranges (128-bit intermediate products)
+ * Errors: EINVAL for zero counts or NULL pointers; ERANGE if P overflows 64 bits.
+ * -------------------------------------------------------------------------- */
+int zero_shard_layout(const uint64_t *numel, uint32_t n_tensors, uint32_t ranks,
+                      uint32_t align_elems, uint64_t *tensor_offset, uint64_t *padded_total,
+                      uint64_t *owner_begin, uint64_t *owner_end);
+
+/* One piece of an owner's work: `len` real elements from flat index `flat`, all
+ * inside tensor `tensor`.  16 bytes; the device step reads an array of these. */
+typedef struct {
+  uint64_t flat;
+  uint32_t len;
+  uint32_t tensor;
+} zero_chunk;
+
+/* ----------------------------------------------------------------------------
+ * zero_chunk_table -- the owner's real elements as a list of chunks.
+ *
+ * The real elements of [begin, end) are the union over tensors of
+ * [tensor_offset[k], tensor_offset[k] + numel[k]) intersected with it (the
+ * padding after each tensor is skipped).  Each intersection is cut at the
+ * flat multiples of `max_chunk_elems`, so interior cuts fall on 128-bit
+ * vector boundaries.  Chunks come out in increasing flat order and cover
+ * every real element of the range exactly once.
+ *
+ * numel, tensor_offset [n_tensors] in: as from zero_shard_layout (offsets
+ *                      increasing, tensors not overlapping)
+ * max_chunk_elems      in : a multiple of 8, at least 8
+ * out[capacity]        out: the chunks; with out == NULL and capacity == 0 only
+ *                      the count is computed (returns ZERO_OK)
+ * n_chunks             out: number of chunks needed, also on ERANGE
+ * Errors: EINVAL (bad sizes, overlapping tensors, begin > end, bad chunk size);
+ *         ERANGE when capacity < *n_chunks (the first `capacity` are written).
+ * -------------------------------------------------------------------------- */
+int zero_chunk_table(const uint64_t *numel, const uint64_t *tensor_offset, uint32_t n_tensors,
+                     uint64_t begin, uint64_t end, uint32_t max_chunk_elems, zero_chunk *out,
+                     uint64_t capacity, uint64_t *n_chunks);
+
+/* Exact byte count num/den, reduced to lowest terms. */
+typedef struct {
+  uint64_t num;
+  uint64_t den;
+} zero_ratio;
+
+/* ----------------------------------------------------------------------------
+ * zero_state_bytes -- idealised persistent bytes per rank.
+ *
+ * [Deep dive] "Count state before choosing a stage" and [ZeRO Q&A] "Memory
+ * Footprint Reduction Matrix": with p, g, o bytes per parameter for the
+ * compute weights, gradients and optimizer state (master + moments),
+ *   out[0] DP     = P (p + g + o)
+ *   out[1] ZeRO-1 = P (p + g) + P o / R
+ *   out[2] ZeRO-2 = P p + P (g + o) / R
+ *   out[3] ZeRO-3 = P (p + g + o) / R
+ * Errors: EINVAL if any count or width is 0 or out is NULL; ERANGE if a
+ * numerator does not fit 64 bits.
+ * -------------------------------------------------------------------------- */
+int zero_state_bytes(uint64_t params, uint64_t ranks, uint32_t param_bytes, uint32_t grad_bytes,
+                     uint32_t optim_bytes, zero_ratio out[4]);
+
+/* ----------------------------------------------------------------------------
+ * zero_reduce_owned -- the owner's reduced gradient, in fp32.
+ *
+ * [Deep dive] "Reduce first, then update the owned slice" (the reference
+ * reduce-scatter: reduce across ranks, keep the owned indices; equally
+ * weighted mean).  For every flat index f in [begin, begin + n):
+ *   s = (accumulate ? out[f - out_base] : +0.0f);
+ *   for r = 0 .. R-1:  s = s + (float) rank_grads[r][f - grad_base];   (fp32)
+ *   out[f - out_base] = s / divisor;                                    (IEEE fp32)
+ * The order is fixed, so results are identical run to run and bit-exact
+ * against a sequential fp32 loop.  A loss scale is folded into `divisor`
+ * (e.g. R * 65536).  R = 1, divisor = 1, accumulate = 1 is fp32 gradient
+ * accumulation (acc += g) of one microstep.
+ *
+ * rank_grads  host array [R] of device pointers; buffer r holds at least
+ *             begin + n - grad_base elements of `grad_dtype` (F16, BF16, F32)
+ * out         device fp32, at least begin + n - out_base elements
+ * d_overflow, d_sumsq: both NULL, or both device pointers; then the pass also
+ *             computes the overflow flag and squared norm of the values it
+ *             writes, exactly as zero_grad_check does (needs `workspace`,
+ *             device, ZERO_CHECK_WS_BYTES bytes, 256-byte aligned).
+ * n == 0 launches nothing (the check outputs are then left untouched).
+ * Errors: EINVAL (R out of [1, ZERO_MAX_RANKS], bad dtype, misaligned pointer
+ *         or base, begin below a base, divisor not finite and > 0, workspace
+ *         missing or too small); EHIP.
+ * -------------------------------------------------------------------------- */
+int zero_reduce_owned(const void *const *rank_grads, uint32_t R, int grad_dtype, uint64_t grad_base,
+                      uint64_t begin, uint64_t n, float divisor, int accumulate, float *out,
+                      uint64_t out_base, int32_t *d_overflow, double *d_sumsq, void *workspace,
+                      size_t ws_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------------------------
+ * zero_grad_check -- overflow flag and squared norm of an fp32 gradient.
+ *
+ * *d_overflow = 1 if any g[i] is infinite or NaN, else 0.
+ * *d_sumsq    = sum of g[i]^2, each square and the sum in fp64 (a fixed
+ *               reduction tree: per-thread sums, wavefront shuffles, an LDS
+ *               block stage, then one block over the per-block partials), so
+ *               the result is identical run to run on one device.  When the
+ *               flag is set the sum is meaningless.
+ * The pages name no overflow handling; with a loss scale the caller skips the
+ * step when the flag is set, and clips with zero_clip_coef otherwise.
+ * g          device fp32 [n];  workspace: device, ZERO_CHECK_WS_BYTES bytes.
+ * n == 0 writes flag 0 and sum 0.
+ * Errors: EINVAL (NULL outputs, workspace too small, misaligned); EHIP.
+ * -------------------------------------------------------------------------- */
+int zero_grad_check(const float *g, uint64_t n, int32_t *d_overflow, double *d_sumsq,
+                    void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------------------------
+ * zero_clip_coef -- host scalar of a global-norm clip:
+ *   *coef = (float) min(1, max_norm / (sqrt(sumsq) + eps))   (fp64, one rounding)
+ * The pages give no clipping rule; this is the common clip_grad_norm_ form.
+ * Errors: EINVAL for a negative or non-finite sumsq, max_norm <= 0, eps < 0.
+ * -------------------------------------------------------------------------- */
+int zero_clip_coef(double sumsq, double max_norm, double eps, float *coef);
+
+/* Arguments of zero_adam_step. */
+typedef struct {
+  /* The owner's work: device chunk table (from zero_chunk_table) and the owner
+   * range [begin, end); chunk pieces outside the range are ignored. */
+  const zero_chunk *chunks;
+  uint64_t n_chunks;
+  uint64_t begin, end;
+  /* Gradient source: either R rank buffers (reduced here, as zero_reduce_owned,
+   * then multiplied by clip_coef) or, with reduced_g != NULL, an owner-local
+   * fp32 reduced gradient (reduced_g[f - local_base]) multiplied by clip_coef. */
+  const void *const *rank_grads; /* host array [R] of device pointers, or NULL */
+  uint32_t R;
+  int32_t grad_dtype;
+  uint64_t grad_base;
+  float divisor;
+  const float *reduced_g;
+  /* fp32 master weights and moments of the owner: element f - local_base,
+   * each at least end - local_base elements. */
+  float *master, *exp_avg, *exp_avg_sq;
+  uint64_t local_base;
+  /* 16-bit compute copy: param16[f - param_base] (F16 or BF16), or ZERO_NONE. */
+  void *param16;
+  int32_t param_dtype;
+  uint64_t param_base;
+  /* Optimizer: step >= 1 counts completed updates including this one. */
+  double lr, beta1, beta2, eps, weight_decay;
+  int32_t adamw; /* 1: decoupled decay (AdamW); 0: classic Adam, wd added to g */
+  uint64_t step;
+  double clip_coef; /* 1.0 when not clipping */
+  uint32_t grid_blocks; /* 0: the library picks the persistent grid */
+} zero_adam_args;
+
+/* ----------------------------------------------------------------------------
+ * zero_adam_step -- fused reduce + Adam/AdamW + 16-bit write-back.
+ *
+ * [Deep dive] "Reduce first, then update the owned slice": for every real
+ * element f of the chunk table (one pass; each byte read and written once):
+ *   g  = reduced gradient (bit-identical to zero_reduce_owned) * clip_coef
+ *   (adamw == 0 and weight_decay != 0: g += weight_decay * w)
+ *   m  = beta1 m + (1 - beta1) g
+ *   v  = beta2 v + (1 - beta2) g^2                 (uncentred)
+ *   w  = w (1 - lr wd [adamw only]) - lr (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+ *   param16[f] = round-to-nearest-even 16-bit copy of w
+ * [ZeRO-3 docs] configuration examples name AdamW with weight_decay; the
+ * pages give no formula, and the decoupled form is used.  Arithmetic is fp32
+ * with constants derived on the host in fp64.
+ * Errors: EINVAL (NULL args, step 0, bad dtype/R/alignment/bases, hyper-
+ * parameters out of range: lr, wd, eps >= 0, betas in [0, 1), divisor > 0,
+ * clip_coef >= 0, all finite); EHIP.  n_chunks == 0 or begin == end is a no-op.
+ * -------------------------------------------------------------------------- */
+int zero_adam_step(const zero_adam_args *args, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_SHARD_H */

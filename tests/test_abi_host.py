@@ -1,0 +1,173 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and its
+host calls (layout, chunk table, state accounting, clip scalar, argument
+validation) agree with the oracle.  No device compute runs here.
+"""
+import ctypes as ct
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import zero_sharded_optimizer_owned_amd as zs
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "zero_shard.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(zero_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert "zero_adam_step" in names and "zero_shard_layout" in names and len(names) >= 8
+    L = ct.CDLL(zs.LIB_PATH)
+    for name in names:
+        assert hasattr(L, name), f"{name} is declared in zero_shard.h but not exported"
+    assert set(names) == set(zs.EXPORTED)
+
+
+def test_layout_matches_oracle():
+    rnd = random.Random(1)
+    for _ in range(400):
+        numels = [rnd.randrange(1, 5000) for _ in range(rnd.randrange(1, 12))]
+        R = rnd.randrange(1, 70)
+        A = rnd.choice([1, 2, 8, 64, 128])
+        off, total, b, e = zs.zero_shard_layout(numels, R, A)
+        ooff, ototal, owners = oracle.layout(numels, R, A)
+        assert list(off) == ooff and total == ototal
+        assert list(zip(b.tolist(), e.tolist())) == owners
+
+
+def test_layout_large_counts_use_wide_products():
+    # 7e10 elements over 64 owners: P * r exceeds 2^64 only for huge P; check the
+    # formula against Python integers near the top of the range too.
+    for P in (70_000_000_000, 2 ** 63 + 12345):
+        off, total, b, e = zs.zero_shard_layout([P], 64, 1)
+        assert total == P
+        assert [int(x) for x in b] == [P * r // 64 for r in range(64)]
+        assert [int(x) for x in e] == [P * (r + 1) // 64 for r in range(64)]
+
+
+def test_layout_errors():
+    with pytest.raises(zs.ZeroShardError) as ei:
+        zs.zero_shard_layout([3, 0], 4, 1)
+    assert ei.value.code == zs.ZERO_EINVAL
+    with pytest.raises(zs.ZeroShardError):
+        zs.zero_shard_layout([3], 0, 1)
+    with pytest.raises(zs.ZeroShardError):
+        zs.zero_shard_layout([3], 4, 0)
+    with pytest.raises(zs.ZeroShardError) as ei:
+        zs.zero_shard_layout([2 ** 63, 2 ** 63], 4, 1)
+    assert ei.value.code == zs.ZERO_ERANGE
+
+
+def test_chunk_table_covers_real_elements_exactly_once():
+    rnd = random.Random(2)
+    for _ in range(300):
+        numels = [rnd.randrange(1, 3000) for _ in range(rnd.randrange(1, 9))]
+        R = rnd.randrange(1, 40)
+        A = rnd.choice([1, 8, 64])
+        C = rnd.choice([8, 64, 512, 4096])
+        off, total, b, e = zs.zero_shard_layout(numels, R, A)
+        for r in range(R):
+            ch = zs.zero_chunk_table(numels, off, int(b[r]), int(e[r]), C)
+            got = [(int(c["flat"]), int(c["flat"]) + int(c["len"])) for c in ch]
+            want = oracle.real_ranges(numels, list(off), int(b[r]), int(e[r]))
+            elems = [f for s, t in got for f in range(s, t)]
+            assert elems == [f for s, t in want for f in range(s, t)]
+            for c in ch:
+                k = int(c["tensor"])
+                assert off[k] <= c["flat"] and c["flat"] + c["len"] <= off[k] + numels[k]
+                assert 1 <= c["len"] <= C
+                # a chunk never crosses a multiple of C
+                assert int(c["flat"]) // C == (int(c["flat"]) + int(c["len"]) - 1) // C
+
+
+def test_chunk_table_capacity_and_errors():
+    numels = [100, 50]
+    off, total, b, e = zs.zero_shard_layout(numels, 1, 8)
+    L = zs.lib()
+    n = np.array(numels, dtype=np.uint64)
+    count = np.zeros(1, dtype=np.uint64)
+    out = np.zeros(2, dtype=zs.CHUNK_DTYPE)
+    rc = L.zero_chunk_table(n.ctypes.data, off.ctypes.data, 2, 0, total, 16, out.ctypes.data, 2,
+                            count.ctypes.data)
+    assert rc == zs.ZERO_ERANGE and int(count[0]) == 7 + 4
+    assert int(out[0]["flat"]) == 0 and int(out[0]["len"]) == 16
+    for C in (0, 7, 12):
+        rc = L.zero_chunk_table(n.ctypes.data, off.ctypes.data, 2, 0, total, C, None, 0,
+                                count.ctypes.data)
+        assert rc == zs.ZERO_EINVAL
+    bad = np.array([0, 90], dtype=np.uint64)  # second tensor overlaps the first
+    assert L.zero_chunk_table(n.ctypes.data, bad.ctypes.data, 2, 0, total, 16, None, 0,
+                              count.ctypes.data) == zs.ZERO_EINVAL
+    assert L.zero_chunk_table(n.ctypes.data, off.ctypes.data, 2, 10, 5, 16, None, 0,
+                              count.ctypes.data) == zs.ZERO_EINVAL
+    assert zs.zero_chunk_table(numels, off, 50, 50, 16).size == 0  # empty owner
+
+
+def test_state_bytes_matches_oracle():
+    rnd = random.Random(3)
+    for _ in range(300):
+        P, R = rnd.randrange(1, 10 ** 13), rnd.randrange(1, 5000)
+        w = [rnd.randrange(1, 20) for _ in range(3)]
+        assert zs.zero_state_bytes(P, R, *w) == oracle.state_bytes(P, R, *w)
+    assert zs.zero_state_bytes(1_500_000_000, 4) == oracle.state_bytes(1_500_000_000, 4)
+
+
+def test_state_bytes_errors():
+    for args in [(0, 4), (5, 0), (5, 4, 0), (5, 4, 2, 0), (5, 4, 2, 2, 0)]:
+        with pytest.raises(zs.ZeroShardError) as ei:
+            zs.zero_state_bytes(*args)
+        assert ei.value.code == zs.ZERO_EINVAL
+    with pytest.raises(zs.ZeroShardError) as ei:
+        zs.zero_state_bytes(2 ** 62, 1, 16, 16, 16)
+    assert ei.value.code == zs.ZERO_ERANGE
+
+
+def test_clip_coef_matches_oracle():
+    for s in (0.0, 0.25, 0.999998, 1.0, 2.0, 1e6, 123.456):
+        assert zs.zero_clip_coef(s) == np.float32(oracle.clip_coef(s))
+    for bad in (-1.0, float("nan"), float("inf")):
+        with pytest.raises(zs.ZeroShardError):
+            zs.zero_clip_coef(bad)
+
+
+def test_device_calls_reject_bad_arguments_before_any_launch():
+    """Validation happens on the host first; these never reach the HIP runtime."""
+    L = zs.lib()
+    a = zs.AdamArgs()
+    a.step = 0
+    assert L.zero_adam_step(ct.byref(a), None) == zs.ZERO_EINVAL
+    assert b"step" in L.zero_last_error()
+    assert L.zero_adam_step(None, None) == zs.ZERO_EINVAL
+    a.step, a.begin, a.end = 1, 10, 5
+    assert L.zero_adam_step(ct.byref(a), None) == zs.ZERO_EINVAL
+    a.begin, a.end = 0, 8
+    a.R = 0
+    assert L.zero_adam_step(ct.byref(a), None) == zs.ZERO_EINVAL
+    ptrs = (ct.c_void_p * 1)(0x1000)
+    out = ct.c_void_p(0x2000)
+    # R out of range, unknown dtype, unaligned pointer, bad divisor, half-given check outputs
+    assert L.zero_reduce_owned(ptrs, 0, zs.ZERO_F16, 0, 0, 8, 1.0, 0, out, 0, None, None, None, 0,
+                               None) == zs.ZERO_EINVAL
+    assert L.zero_reduce_owned(ptrs, 1, 9, 0, 0, 8, 1.0, 0, out, 0, None, None, None, 0,
+                               None) == zs.ZERO_EINVAL
+    bad = (ct.c_void_p * 1)(0x1002)
+    assert L.zero_reduce_owned(bad, 1, zs.ZERO_F16, 0, 0, 8, 1.0, 0, out, 0, None, None, None, 0,
+                               None) == zs.ZERO_EINVAL
+    assert L.zero_reduce_owned(ptrs, 1, zs.ZERO_F16, 0, 0, 8, 0.0, 0, out, 0, None, None, None, 0,
+                               None) == zs.ZERO_EINVAL
+    assert L.zero_reduce_owned(ptrs, 1, zs.ZERO_F16, 4, 4, 8, 1.0, 0, out, 0, None, None, None, 0,
+                               None) == zs.ZERO_EINVAL  # base not a multiple of 8
+    assert L.zero_reduce_owned(ptrs, 1, zs.ZERO_F16, 0, 0, 8, 1.0, 0, out, 0, ct.c_void_p(0x3000),
+                               None, None, 0, None) == zs.ZERO_EINVAL
+    assert L.zero_reduce_owned(ptrs, 1, zs.ZERO_F16, 0, 0, 8, 1.0, 0, out, 0, ct.c_void_p(0x3000),
+                               ct.c_void_p(0x4000), ct.c_void_p(0x10000), 100,
+                               None) == zs.ZERO_EINVAL  # workspace too small
+    assert L.zero_grad_check(None, 0, None, None, None, 0, None) == zs.ZERO_EINVAL

@@ -1,0 +1,355 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by
+element, on seeded inputs that span many vectors, chunks and ragged ends.
+
+Reduced gradients, overflow flags and the input generator: bit-exact.
+Master weights and moments: |gpu - oracle| <= 1e-7 + 1e-6 |oracle| after each
+step.  16-bit copies: within 1 ulp of the oracle's rounding of its own master
+weight.  Squared norms: 1e-9 relative.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import (BF16, F16, F32, assert_bits_equal, assert_p16_within_ulp, assert_state_close,
+                     from_dev, gen, to_dev)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import zero_sharded_optimizer_owned_amd as zs  # noqa: E402
+
+DEV = "cuda"
+HP = dict(lr=1e-3, beta1=0.8, beta2=0.999, eps=1e-8, weight_decay=3e-7, adamw=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    zs.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- generator
+@pytest.mark.parametrize("code", [F16, BF16, F32])
+@pytest.mark.parametrize("dist,scale", [(synth.DIST_NORMAL, 1e-3), (synth.DIST_NORMAL, 65.536),
+                                        (synth.DIST_UNIFORM, 0.3), (synth.DIST_SQUARE, 1e-4)])
+def test_device_generator_matches_host(code, dist, scale):
+    n, i0 = 100_003, 12_345
+    key = synth.stream_key(7, synth.STREAM_GRAD, 3, 2)
+    t = torch.empty(n, dtype={F16: torch.float16, BF16: torch.bfloat16, F32: torch.float32}[code],
+                    device=DEV)
+    synth.device_fill(t, key, i0, dist, scale)
+    torch.cuda.synchronize()
+    want = synth.values(key, synth.arange(i0, i0 + n), dist, scale, code)
+    assert_bits_equal(from_dev(t), want, "device generator")
+
+
+# ---------------------------------------------------------------- reduce
+def _rank_inputs(code, R, total, seed=1, scale=1e-3):
+    return [gen(seed, synth.STREAM_GRAD, total, synth.DIST_NORMAL, scale, code, rank=r) for r in range(R)]
+
+
+@pytest.mark.parametrize("code", [F16, BF16, F32])
+@pytest.mark.parametrize("R", [1, 3, 4, 8, 13, 64])
+def test_reduce_bitexact(code, R):
+    total = 70_001
+    begin, n = 13, 50_005          # ragged on both ends
+    grads = _rank_inputs(code, R, total, seed=R)
+    dgr = [to_dev(g, code) for g in grads]
+    for divisor in (float(R), float(R) * 65536.0, 3.0):
+        out_base = begin & ~7
+        out = torch.full((begin + n - out_base + 16,), 7.0, dtype=torch.float32, device=DEV)
+        zs.zero_reduce_owned(dgr, begin, n, divisor, out, out_base=out_base)
+        got = from_dev(out)
+        want = oracle.reduce([g[begin:begin + n] for g in grads], code, divisor)
+        assert_bits_equal(got[begin - out_base:begin - out_base + n], want, f"R={R} D={divisor}")
+        assert np.all(got[:begin - out_base] == 7.0) and np.all(got[begin - out_base + n:] == 7.0)
+
+
+@pytest.mark.parametrize("code", [F16, BF16, F32])
+def test_reduce_accumulate_and_slices(code):
+    """Owner-local rank slices (grad_base = local_base) and accumulation into out."""
+    R, total = 5, 40_000
+    begin, end = 1234 + 3, 33_333
+    lb = begin & ~7
+    grads = _rank_inputs(code, R, total, seed=11)
+    slices = [to_dev(g[lb:end], code) for g in grads]
+    start = gen(2, synth.STREAM_EXP_AVG, end - lb, synth.DIST_NORMAL, 1e-2, F32)
+    out = to_dev(start.copy(), F32)
+    zs.zero_reduce_owned(slices, begin, end - begin, 1.0, out, grad_base=lb, out_base=lb,
+                         accumulate=True)
+    want = start.copy()
+    oracle.reduce([g[begin:end] for g in grads], code, 1.0, out=want[begin - lb:], accumulate=True)
+    assert_bits_equal(from_dev(out), want, "accumulate")
+
+
+def test_negative_zero_and_specials():
+    n = 64
+    neg0 = np.full(n, 0x8000, dtype=np.uint16)
+    out = torch.empty(n, dtype=torch.float32, device=DEV)
+    zs.zero_reduce_owned([to_dev(neg0, F16)] * 3, 0, n, 4.0, out)
+    got = from_dev(out)
+    assert np.all(got == 0) and not np.any(np.signbit(got))
+    big = np.array([3e38] * 8 + [1e8, 1.0, -1e8] + [0.0] * 5, dtype=np.float32)
+    rows = [big, big, -big]
+    out = torch.empty(16, dtype=torch.float32, device=DEV)
+    zs.zero_reduce_owned([to_dev(r, F32) for r in rows], 0, 16, 1.0, out)
+    assert_bits_equal(from_dev(out), oracle.reduce(rows, F32, 1.0), "specials")
+
+
+def _check_bufs():
+    return (torch.zeros(1, dtype=torch.int32, device=DEV), torch.zeros(1, dtype=torch.float64, device=DEV),
+            zs.check_workspace(DEV))
+
+
+@pytest.mark.parametrize("code", [F16, BF16])
+def test_reduce_fused_check(code):
+    R, total = 8, 300_007
+    begin, n = 5, 300_000
+    grads = _rank_inputs(code, R, total, seed=3, scale=65.536)
+    dgr = [to_dev(g, code) for g in grads]
+    D = float(R) * 65536.0
+    ov, ss, ws = _check_bufs()
+    out = torch.empty(begin + n, dtype=torch.float32, device=DEV)
+    zs.zero_reduce_owned(dgr, begin, n, D, out, check=(ov, ss, ws))
+    want = oracle.reduce([g[begin:begin + n] for g in grads], code, D)
+    assert_bits_equal(from_dev(out)[begin:], want, "fused reduce")
+    flag, sumsq = oracle.grad_check(want)
+    assert int(ov.item()) == flag == 0
+    assert math.isclose(ss.item(), sumsq, rel_tol=1e-9)
+    first = ss.item()
+    zs.zero_reduce_owned(dgr, begin, n, D, out, check=(ov, ss, ws))
+    assert ss.item() == first  # run to run identical
+
+
+@pytest.mark.parametrize("pos", [0, 3, 7, 8, 100_003, 299_999])
+@pytest.mark.parametrize("kind", ["inf", "nan", "pm_inf"])
+def test_overflow_flag_positions(pos, kind):
+    R, n, begin = 4, 300_000, 5
+    grads = _rank_inputs(F16, R, begin + n, seed=4, scale=65.536)
+    f = begin + pos
+    if kind == "inf":
+        grads[2][f] = 0x7C00
+    elif kind == "nan":
+        grads[R - 1][f] = 0x7E00
+    else:  # +inf in one rank and -inf in another: their sum is NaN
+        grads[0][f], grads[1][f] = 0x7C00, 0xFC00
+    dgr = [to_dev(g, F16) for g in grads]
+    ov, ss, ws = _check_bufs()
+    out = torch.empty(begin + n, dtype=torch.float32, device=DEV)
+    zs.zero_reduce_owned(dgr, begin, n, float(R) * 65536, out, check=(ov, ss, ws))
+    want = oracle.reduce([g[begin:] for g in grads], F16, float(R) * 65536)
+    assert_bits_equal(from_dev(out)[begin:], want, "reduce with non-finite input")
+    assert int(ov.item()) == oracle.grad_check(want)[0] == 1
+
+
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 1000, 65_537, 1_000_003])
+def test_grad_check_standalone(n):
+    g = gen(5, synth.STREAM_GRAD, max(n, 1), synth.DIST_NORMAL, 1e-3, F32)[:n]
+    ov, ss, ws = _check_bufs()
+    ov.fill_(9)
+    ss.fill_(-1)
+    zs.zero_grad_check(to_dev(g, F32) if n else torch.empty(0, dtype=torch.float32, device=DEV),
+                       ov, ss, ws)
+    flag, sumsq = oracle.grad_check(g)
+    assert int(ov.item()) == flag
+    assert math.isclose(ss.item(), sumsq, rel_tol=1e-9, abs_tol=0.0)
+    if n:
+        g2 = g.copy()
+        g2[n // 2] = np.inf
+        zs.zero_grad_check(to_dev(g2, F32), ov, ss, ws)
+        assert int(ov.item()) == 1
+
+
+# ---------------------------------------------------------------- fused step
+LAYOUTS = {
+    "ragged": ([1000, 37, 5003, 1, 64, 777, 4096, 9, 20_000], 3, 64),
+    "tiny_tensors": ([1, 2, 3, 5, 7, 8, 9, 15, 16, 17, 31, 33, 63, 64, 65, 100] * 6, 5, 8),
+    "empty_owners": ([3, 2], 9, 1),
+    "one_big": ([123_457], 4, 64),
+}
+
+
+def _owner_inputs(numels, R, A, owner, gcode, seed):
+    off, total, b, e = zs.zero_shard_layout(numels, R, A)
+    begin, end = int(b[owner]), int(e[owner])
+    lb = begin & ~7
+    grads = _rank_inputs(gcode, R, total, seed=seed)
+    size = max(8, end - lb)
+    w = gen(seed, synth.STREAM_MASTER, size, synth.DIST_NORMAL, 0.02, F32)
+    m = gen(seed, synth.STREAM_EXP_AVG, size, synth.DIST_NORMAL, 5e-4, F32)
+    v = gen(seed, synth.STREAM_EXP_AVG_SQ, size, synth.DIST_SQUARE, 1e-4, F32)
+    return off, total, begin, end, lb, grads, w, m, v
+
+
+@pytest.mark.parametrize("layout", list(LAYOUTS))
+@pytest.mark.parametrize("gcode,pcode", [(F16, F16), (BF16, BF16), (F32, BF16), (F32, 0), (F16, BF16)])
+@pytest.mark.parametrize("max_chunk", [64, 2048])
+def test_adam_step_matches_oracle(layout, gcode, pcode, max_chunk):
+    numels, R, A = LAYOUTS[layout]
+    for owner in range(R):
+        off, total, begin, end, lb, grads, w, m, v = _owner_inputs(numels, R, A, owner, gcode, owner + 1)
+        chunks = zs.zero_chunk_table(numels, off, begin, end, max_chunk)
+        dchunks = zs.chunks_to_device(chunks) if chunks.size else None
+        dgr = [to_dev(g, gcode) for g in grads]
+        dw, dm, dv = to_dev(w, F32), to_dev(m, F32), to_dev(v, F32)
+        sentinel = 0x7BFF if pcode == F16 else 0x3F80
+        p16_host = np.full(total + 8, sentinel, dtype=np.uint16)
+        dp = to_dev(p16_host, pcode) if pcode else None
+        ow, om, ov_ = w.copy(), m.copy(), v.copy()
+        ranges = oracle.real_ranges(numels, list(off), begin, end)
+        for t in (11, 12, 13):  # independent trajectories, three steps
+            zs.zero_adam_step(chunks_dev=dchunks, n_chunks=chunks.size, begin=begin, end=end,
+                              master=dw, exp_avg=dm, exp_avg_sq=dv, local_base=lb, step=t,
+                              rank_grads=dgr, divisor=float(R), param16=dp, **HP)
+            oracle.owner_step(ranges, oracle.hyper(step=t, **HP), ow, om, ov_, lb, grads=grads,
+                              gdtype=gcode, divisor=float(R), p16=p16_host if pcode else None,
+                              pdtype=pcode)
+            what = f"{layout} owner {owner} step {t}"
+            assert_state_close(from_dev(dw), ow, what + " w")
+            assert_state_close(from_dev(dm), om, what + " m")
+            assert_state_close(from_dev(dv), ov_, what + " v")
+            if pcode:
+                got = from_dev(dp)
+                real = np.zeros(total + 8, dtype=bool)
+                for s, e_ in ranges:
+                    real[s:e_] = True
+                assert np.all(got[~real] == sentinel), what + ": padding or foreign elements written"
+                assert_p16_within_ulp(got[real], p16_host[real], what + " p16")
+
+
+@pytest.mark.parametrize("adamw,wd", [(False, 0.05), (False, 0.0), (True, 0.01)])
+def test_adam_variants(adamw, wd):
+    numels, R, A = [4099, 17, 333], 2, 8
+    hp = dict(HP, adamw=adamw, weight_decay=wd)
+    off, total, begin, end, lb, grads, w, m, v = _owner_inputs(numels, R, A, 1, F16, 9)
+    chunks = zs.zero_chunk_table(numels, off, begin, end, 512)
+    dw, dm, dv = to_dev(w, F32), to_dev(m, F32), to_dev(v, F32)
+    zs.zero_adam_step(chunks_dev=zs.chunks_to_device(chunks), n_chunks=chunks.size, begin=begin,
+                      end=end, master=dw, exp_avg=dm, exp_avg_sq=dv, local_base=lb, step=3,
+                      rank_grads=[to_dev(g, F16) for g in grads], divisor=2.0, **hp)
+    ranges = oracle.real_ranges(numels, list(off), begin, end)
+    oracle.owner_step(ranges, oracle.hyper(step=3, **hp), w, m, v, lb, grads=grads, gdtype=F16,
+                      divisor=2.0)
+    assert_state_close(from_dev(dw), w, "w")
+    assert_state_close(from_dev(dm), m, "m")
+    assert_state_close(from_dev(dv), v, "v")
+
+
+def test_two_pass_with_clip_matches_oracle_and_fused():
+    """reduce (+check) -> adam from the reduced gradient with a clip factor."""
+    numels, R, A = [50_000, 1234, 77_777], 4, 64
+    off, total, begin, end, lb, grads, w, m, v = _owner_inputs(numels, R, A, 2, F16, 21)
+    dgr = [to_dev(g, F16) for g in grads]
+    chunks = zs.zero_chunk_table(numels, off, begin, end, 4096)
+    dch = zs.chunks_to_device(chunks)
+    g_dev = torch.zeros(end - lb, dtype=torch.float32, device=DEV)
+    ov, ss, ws = _check_bufs()
+    zs.zero_reduce_owned(dgr, begin, end - begin, float(R), g_dev, out_base=lb, check=(ov, ss, ws))
+    coef = 0.37
+    dw, dm, dv = to_dev(w, F32), to_dev(m, F32), to_dev(v, F32)
+    dp = torch.zeros(total, dtype=torch.float16, device=DEV)
+    zs.zero_adam_step(chunks_dev=dch, n_chunks=chunks.size, begin=begin, end=end, master=dw,
+                      exp_avg=dm, exp_avg_sq=dv, local_base=lb, step=5, reduced_g=g_dev,
+                      param16=dp, clip_coef=coef, **HP)
+    g_or = np.zeros(end - lb, dtype=np.float32)
+    g_or[begin - lb:] = oracle.reduce([g[begin:end] for g in grads], F16, float(R))
+    assert_bits_equal(from_dev(g_dev)[begin - lb:], g_or[begin - lb:], "two-pass reduce")
+    ranges = oracle.real_ranges(numels, list(off), begin, end)
+    ow, om, ovv = w.copy(), m.copy(), v.copy()
+    p_or = np.zeros(total, dtype=np.uint16)
+    oracle.owner_step(ranges, oracle.hyper(step=5, clip_coef=coef, **HP), ow, om, ovv, lb,
+                      reduced_g=g_or, p16=p_or, pdtype=F16)
+    assert_state_close(from_dev(dw), ow, "w")
+    assert_state_close(from_dev(dm), om, "m")
+    assert_state_close(from_dev(dv), ovv, "v")
+    assert_p16_within_ulp(from_dev(dp), p_or, "p16")
+    # the fused single pass gives the same bits as reduce-then-step with coef 1
+    fw, fm, fv = to_dev(w, F32), to_dev(m, F32), to_dev(v, F32)
+    tw, tm, tv = to_dev(w, F32), to_dev(m, F32), to_dev(v, F32)
+    zs.zero_adam_step(chunks_dev=dch, n_chunks=chunks.size, begin=begin, end=end, master=fw,
+                      exp_avg=fm, exp_avg_sq=fv, local_base=lb, step=5, rank_grads=dgr,
+                      divisor=float(R), **HP)
+    zs.zero_adam_step(chunks_dev=dch, n_chunks=chunks.size, begin=begin, end=end, master=tw,
+                      exp_avg=tm, exp_avg_sq=tv, local_base=lb, step=5, reduced_g=g_dev, **HP)
+    for a, b in ((fw, tw), (fm, tm), (fv, tv)):
+        assert_bits_equal(from_dev(a), from_dev(b), "fused vs two-pass")
+
+
+def test_no_op_cases_leave_memory_untouched():
+    dw = torch.full((16,), 3.0, device=DEV)
+    dm, dv = torch.zeros(16, device=DEV), torch.zeros(16, device=DEV)
+    g = torch.ones(16, dtype=torch.float16, device=DEV)
+    zs.zero_adam_step(chunks_dev=None, n_chunks=0, begin=8, end=8, master=dw, exp_avg=dm,
+                      exp_avg_sq=dv, local_base=8, step=1, rank_grads=[g], divisor=1.0, **HP)
+    out = torch.full((16,), 5.0, device=DEV)
+    zs.zero_reduce_owned([g], 3, 0, 1.0, out)
+    torch.cuda.synchronize()
+    assert torch.all(dw == 3.0) and torch.all(out == 5.0)
+
+
+def test_max_ranks():
+    R, n = zs.ZERO_MAX_RANKS, 1000
+    grads = [gen(8, synth.STREAM_GRAD, n, synth.DIST_NORMAL, 1.0, BF16, rank=r) for r in range(R)]
+    out = torch.empty(n, dtype=torch.float32, device=DEV)
+    zs.zero_reduce_owned([to_dev(g, BF16) for g in grads], 0, n, float(R), out)
+    assert_bits_equal(from_dev(out), oracle.reduce(grads, BF16, float(R)), "R=256")
+    with pytest.raises(zs.ZeroShardError):
+        zs.zero_reduce_owned([to_dev(grads[0], BF16)] * (R + 1), 0, n, 1.0, out)
+
+
+# ---------------------------------------------------------------- the pages' tiny case
+def _tiny_run(owners, grads_fn, steps=5):
+    P, R = 11, 4
+    hp = dict(lr=0.01, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, adamw=False)
+    w = torch.tensor([0.1 * i for i in range(P)] + [0.0] * 5, dtype=torch.float32, device=DEV)
+    m, v = torch.zeros(16, device=DEV), torch.zeros(16, device=DEV)
+    for t in range(1, steps + 1):
+        rows = [to_dev(np.array([grads_fn(i, r, t) for i in range(P)] + [0.0] * 5, dtype=np.float32), F32)
+                for r in range(R)]
+        for b, e in owners:
+            if b == e:
+                continue
+            lb = b & ~7
+            ch = zs.zero_chunk_table([P], [0], b, e, 8)
+            zs.zero_adam_step(chunks_dev=zs.chunks_to_device(ch), n_chunks=ch.size, begin=b, end=e,
+                              master=w[lb:], exp_avg=m[lb:], exp_avg_sq=v[lb:], local_base=lb,
+                              step=t, rank_grads=rows, divisor=float(R), max_flat=e, **hp)
+    return from_dev(w)[:P], from_dev(m)[:P], from_dev(v)[:P]
+
+
+def _uniform_grad(i, r, t):
+    key = synth.stream_key(1, synth.STREAM_GRAD, r, t)
+    return float(synth.values_f32(key, [i], synth.DIST_UNIFORM, 0.3)[0])
+
+
+@pytest.mark.parametrize("grad_fn", [oracle.pages_gradient, _uniform_grad])
+def test_tiny_sharded_equals_unsharded_on_gpu(grad_fn):
+    owners = [(o.start, o.stop) for o in oracle.owner_ranges(11, 4)]
+    sharded = _tiny_run(owners, grad_fn)
+    unsharded = _tiny_run([(0, 11)], grad_fn)
+    for a, b in zip(sharded, unsharded):
+        assert_bits_equal(a, b, "sharded vs unsharded")
+    reference, _ = oracle.compare_owned_updates(11, 4, 5, grad=grad_fn)
+    ref = np.array(reference)
+    for k in range(3):
+        assert_state_close(sharded[k], ref[:, k].astype(np.float32), f"vs the pages' lab, field {k}")
+
+
+def test_first_step_closed_form_on_gpu():
+    # w = 1, gradient 2, lr 0.01, t = 1: w = 1 - 0.01 * 2 / (2 + 1e-8), m = 0.2, v = 0.004
+    w = torch.ones(8, device=DEV)
+    m, v = torch.zeros(8, device=DEV), torch.zeros(8, device=DEV)
+    g = torch.full((8,), 2.0, device=DEV)
+    ch = zs.zero_chunk_table([8], [0], 0, 8, 8)
+    zs.zero_adam_step(chunks_dev=zs.chunks_to_device(ch), n_chunks=1, begin=0, end=8, master=w,
+                      exp_avg=m, exp_avg_sq=v, local_base=0, step=1, rank_grads=[g], divisor=1.0,
+                      lr=0.01, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, adamw=False)
+    assert_state_close(from_dev(w), np.full(8, 1.0 - 0.01 * 2.0 / (2.0 + 1e-8)), "w")
+    assert_state_close(from_dev(m), np.full(8, 0.2), "m")
+    assert_state_close(from_dev(v), np.full(8, 0.004), "v")

@@ -1,0 +1,323 @@
+"""ZeRO owner-shard optimizer step on one MI355X: Python binding of libzero_shard.so.
+
+Argument marshalling only.  Every step of the path runs in the HIP library
+(``csrc/device.hip``, ``csrc/host.cpp``; C ABI in ``include/zero_shard.h``);
+this module turns torch tensors into pointers, checks devices, dtypes,
+contiguity and extents against what the kernels will touch, passes torch's
+current stream, and raises on error codes.  There is no fallback: if the
+library is missing, every call raises.
+
+The functions carry the names of the C entry points.  ``OwnerShard`` bundles
+one owner's layout, device chunk table and fp32 state for convenience; its
+methods are sequences of the same calls.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+from fractions import Fraction
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from .build import LIB_PATH, build
+
+ZERO_OK, ZERO_EINVAL, ZERO_ERANGE, ZERO_EHIP = 0, -1, -2, -3
+ZERO_NONE, ZERO_F16, ZERO_BF16, ZERO_F32 = 0, 1, 2, 3
+ZERO_MAX_RANKS = 256
+ZERO_CHECK_WS_BYTES = 65536
+
+EXPORTED = ("zero_last_error", "zero_shard_layout", "zero_chunk_table", "zero_state_bytes",
+            "zero_reduce_owned", "zero_grad_check", "zero_clip_coef", "zero_adam_step")
+
+CHUNK_DTYPE = np.dtype([("flat", "<u8"), ("len", "<u4"), ("tensor", "<u4")])
+
+
+class ZeroShardError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class AdamArgs(ct.Structure):
+    _fields_ = [
+        ("chunks", ct.c_void_p), ("n_chunks", ct.c_uint64), ("begin", ct.c_uint64),
+        ("end", ct.c_uint64),
+        ("rank_grads", ct.c_void_p), ("R", ct.c_uint32), ("grad_dtype", ct.c_int32),
+        ("grad_base", ct.c_uint64), ("divisor", ct.c_float), ("reduced_g", ct.c_void_p),
+        ("master", ct.c_void_p), ("exp_avg", ct.c_void_p), ("exp_avg_sq", ct.c_void_p),
+        ("local_base", ct.c_uint64),
+        ("param16", ct.c_void_p), ("param_dtype", ct.c_int32), ("param_base", ct.c_uint64),
+        ("lr", ct.c_double), ("beta1", ct.c_double), ("beta2", ct.c_double), ("eps", ct.c_double),
+        ("weight_decay", ct.c_double), ("adamw", ct.c_int32), ("step", ct.c_uint64),
+        ("clip_coef", ct.c_double), ("grid_blocks", ct.c_uint32),
+    ]
+
+
+class Ratio(ct.Structure):
+    _fields_ = [("num", ct.c_uint64), ("den", ct.c_uint64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                               "(there is no fallback path)")
+        L = ct.CDLL(LIB_PATH)
+        P, U32, U64, I, F, D = ct.c_void_p, ct.c_uint32, ct.c_uint64, ct.c_int, ct.c_float, ct.c_double
+        L.zero_last_error.restype = ct.c_char_p
+        L.zero_last_error.argtypes = []
+        for name in EXPORTED[1:]:
+            getattr(L, name).restype = I
+        L.zero_shard_layout.argtypes = [P, U32, U32, U32, P, P, P, P]
+        L.zero_chunk_table.argtypes = [P, P, U32, U64, U64, U32, P, U64, P]
+        L.zero_state_bytes.argtypes = [U64, U64, U32, U32, U32, P]
+        L.zero_reduce_owned.argtypes = [P, U32, I, U64, U64, U64, F, I, P, U64, P, P, P, ct.c_size_t, P]
+        L.zero_grad_check.argtypes = [P, U64, P, P, P, ct.c_size_t, P]
+        L.zero_clip_coef.argtypes = [D, D, D, ct.POINTER(F)]
+        L.zero_adam_step.argtypes = [ct.POINTER(AdamArgs), P]
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != ZERO_OK:
+        raise ZeroShardError(rc, lib().zero_last_error().decode())
+
+
+def _u64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.uint64))
+
+
+def _p(a: np.ndarray):
+    return ct.c_void_p(a.ctypes.data) if a is not None and a.size else None
+
+
+# ---------------------------------------------------------------- host calls
+def zero_shard_layout(numels: Sequence[int], ranks: int, align: int):
+    """(tensor offsets, padded total, owner begins, owner ends) of the flat buffer."""
+    n = _u64(numels)
+    off = np.zeros(max(1, n.size), dtype=np.uint64)
+    total = np.zeros(1, dtype=np.uint64)
+    b = np.zeros(max(1, ranks), dtype=np.uint64)
+    e = np.zeros(max(1, ranks), dtype=np.uint64)
+    _check(lib().zero_shard_layout(_p(n), n.size, ranks, align, _p(off), _p(total), _p(b), _p(e)))
+    return off[: n.size], int(total[0]), b[:ranks], e[:ranks]
+
+
+def zero_chunk_table(numels: Sequence[int], offsets: Sequence[int], begin: int, end: int,
+                     max_chunk: int) -> np.ndarray:
+    """The owner's chunks as a structured array (flat, len, tensor)."""
+    n, off = _u64(numels), _u64(offsets)
+    if n.size != off.size:
+        raise ValueError("numels and offsets differ in length")
+    count = np.zeros(1, dtype=np.uint64)
+    _check(lib().zero_chunk_table(_p(n), _p(off), n.size, begin, end, max_chunk, None, 0, _p(count)))
+    out = np.zeros(int(count[0]), dtype=CHUNK_DTYPE)
+    _check(lib().zero_chunk_table(_p(n), _p(off), n.size, begin, end, max_chunk,
+                                  _p(out) if out.size else None, out.size, _p(count)))
+    return out
+
+
+def zero_state_bytes(params: int, ranks: int, param: int = 2, grad: int = 2,
+                     optimizer: int = 12) -> dict:
+    out = (Ratio * 4)()
+    _check(lib().zero_state_bytes(params, ranks, param, grad, optimizer, out))
+    names = ("DP", "ZeRO-1", "ZeRO-2", "ZeRO-3")
+    return {k: Fraction(out[i].num, out[i].den) for i, k in enumerate(names)}
+
+
+def zero_clip_coef(sumsq: float, max_norm: float = 1.0, eps: float = 1e-6) -> float:
+    c = ct.c_float()
+    _check(lib().zero_clip_coef(sumsq, max_norm, eps, ct.byref(c)))
+    return c.value
+
+
+# ---------------------------------------------------------------- device calls
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    return {torch.float16: ZERO_F16, torch.bfloat16: ZERO_BF16, torch.float32: ZERO_F32}[t.dtype]
+
+
+def _dev(t, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _stream():
+    return ct.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _need(t, name: str, elems: int) -> None:
+    if t.numel() < elems:
+        raise ValueError(f"{name} holds {t.numel()} elements, {elems} needed")
+
+
+def _rank_ptrs(rank_grads, base: int, last: int, name="rank_grads"):
+    if not rank_grads:
+        raise ValueError("no rank buffers")
+    dt = rank_grads[0].dtype
+    dev = rank_grads[0].device
+    arr = (ct.c_void_p * len(rank_grads))()
+    for r, g in enumerate(rank_grads):
+        _dev(g, f"{name}[{r}]", dt)
+        if g.device != dev:
+            raise ValueError("rank buffers on different devices")
+        _need(g, f"{name}[{r}]", last - base)
+        arr[r] = g.data_ptr()
+    return arr, _dtype_code(rank_grads[0])
+
+
+def zero_reduce_owned(rank_grads, begin: int, n: int, divisor: float, out, *, grad_base: int = 0,
+                      out_base: int = 0, accumulate: bool = False, check=None) -> None:
+    """out[f - out_base] = (start + sum_r rank_grads[r][f - grad_base]) / divisor, f in [begin, begin+n).
+
+    ``check`` = (overflow int32[1], sumsq float64[1], workspace uint8[>=64 KiB]) device
+    tensors to also compute the overflow flag and squared norm in the same pass.
+    """
+    torch = _torch()
+    arr, code = _rank_ptrs(rank_grads, grad_base, begin + n)
+    _dev(out, "out", torch.float32)
+    _need(out, "out", begin + n - out_base)
+    ov = ss = ws = None
+    ws_bytes = 0
+    if check is not None:
+        ov, ss, ws = check
+        _dev(ov, "overflow", torch.int32)
+        _dev(ss, "sumsq", torch.float64)
+        _dev(ws, "workspace")
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib().zero_reduce_owned(
+        arr, len(rank_grads), code, grad_base, begin, n, divisor, int(accumulate),
+        ct.c_void_p(out.data_ptr()), out_base,
+        ct.c_void_p(ov.data_ptr()) if ov is not None else None,
+        ct.c_void_p(ss.data_ptr()) if ss is not None else None,
+        ct.c_void_p(ws.data_ptr()) if ws is not None else None, ws_bytes, _stream()))
+
+
+def zero_grad_check(g, overflow, sumsq, workspace) -> None:
+    torch = _torch()
+    _dev(g, "g", torch.float32)
+    _dev(overflow, "overflow", torch.int32)
+    _dev(sumsq, "sumsq", torch.float64)
+    _dev(workspace, "workspace")
+    _check(lib().zero_grad_check(
+        ct.c_void_p(g.data_ptr()), g.numel(), ct.c_void_p(overflow.data_ptr()),
+        ct.c_void_p(sumsq.data_ptr()), ct.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), _stream()))
+
+
+def check_workspace(device=None):
+    """A device buffer of ZERO_CHECK_WS_BYTES bytes for the overflow / norm reduction."""
+    torch = _torch()
+    return torch.empty(ZERO_CHECK_WS_BYTES, dtype=torch.uint8, device=device or "cuda")
+
+
+def chunks_to_device(chunks: np.ndarray, device=None):
+    torch = _torch()
+    flat = np.ascontiguousarray(chunks).view(np.uint8)
+    t = torch.from_numpy(flat.copy()).to(device or "cuda")
+    return t
+
+
+def zero_adam_step(*, chunks_dev, n_chunks: int, begin: int, end: int, master, exp_avg, exp_avg_sq,
+                   local_base: int, step: int, lr: float, beta1: float, beta2: float, eps: float,
+                   weight_decay: float = 0.0, adamw: bool = True, rank_grads=None, grad_base: int = 0,
+                   divisor: float = 1.0, reduced_g=None, param16=None, param_base: int = 0,
+                   clip_coef: float = 1.0, grid_blocks: int = 0, max_flat: Optional[int] = None) -> None:
+    """Fused reduce + Adam/AdamW + 16-bit write-back over a device chunk table.
+
+    ``max_flat`` (default ``end``) bounds the flat indices the chunk table may
+    name; every buffer is checked to hold them.
+    """
+    torch = _torch()
+    last = end if max_flat is None else max_flat
+    if chunks_dev is not None:
+        _dev(chunks_dev, "chunks")
+        if chunks_dev.numel() * chunks_dev.element_size() < n_chunks * CHUNK_DTYPE.itemsize:
+            raise ValueError("chunk table smaller than n_chunks")
+    for name, t in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        _dev(t, name, torch.float32)
+        _need(t, name, last - local_base)
+    a = AdamArgs()
+    a.chunks = chunks_dev.data_ptr() if chunks_dev is not None else None
+    a.n_chunks, a.begin, a.end = n_chunks, begin, end
+    keep = None
+    if reduced_g is not None:
+        _dev(reduced_g, "reduced_g", torch.float32)
+        _need(reduced_g, "reduced_g", last - local_base)
+        a.reduced_g = reduced_g.data_ptr()
+    else:
+        keep, code = _rank_ptrs(rank_grads, grad_base, last)
+        a.rank_grads = ct.cast(keep, ct.c_void_p)
+        a.R, a.grad_dtype, a.grad_base = len(rank_grads), code, grad_base
+    a.divisor = divisor
+    a.master, a.exp_avg, a.exp_avg_sq = master.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr()
+    a.local_base = local_base
+    if param16 is not None:
+        _dev(param16, "param16")
+        if param16.dtype not in (torch.float16, torch.bfloat16):
+            raise TypeError("param16 must be float16 or bfloat16")
+        _need(param16, "param16", last - param_base)
+        a.param16, a.param_dtype, a.param_base = param16.data_ptr(), _dtype_code(param16), param_base
+    a.lr, a.beta1, a.beta2, a.eps, a.weight_decay = lr, beta1, beta2, eps, weight_decay
+    a.adamw, a.step, a.clip_coef, a.grid_blocks = int(adamw), step, clip_coef, grid_blocks
+    _check(lib().zero_adam_step(ct.byref(a), _stream()))
+    del keep
+
+
+# ---------------------------------------------------------------- convenience
+class OwnerShard:
+    """One owner's layout, device chunk table and fp32 master/moment state.
+
+    Owner-local arrays start at ``local_base = begin & ~7`` and hold
+    ``end - local_base`` elements, so their 128-bit vectors line up with the
+    flat buffer's.
+    """
+
+    def __init__(self, numels: Sequence[int], ranks: int, owner: int, align: int = 64,
+                 max_chunk: int = 16384, device=None):
+        torch = _torch()
+        self.numels = [int(x) for x in numels]
+        self.offsets, self.padded_total, begins, ends = zero_shard_layout(self.numels, ranks, align)
+        self.ranks, self.owner = ranks, owner
+        self.begin, self.end = int(begins[owner]), int(ends[owner])
+        self.local_base = self.begin & ~7
+        self.local_size = self.end - self.local_base
+        self.chunks = zero_chunk_table(self.numels, self.offsets, self.begin, self.end, max_chunk)
+        self.device = torch.device(device or "cuda")
+        self.chunks_dev = chunks_to_device(self.chunks, self.device)
+        self.n_real = int(self.chunks["len"].sum()) if self.chunks.size else 0
+        self.step_count = 0
+
+    def alloc_state(self):
+        torch = _torch()
+        mk = lambda: torch.zeros(max(8, self.local_size), dtype=torch.float32, device=self.device)
+        self.master, self.exp_avg, self.exp_avg_sq = mk(), mk(), mk()
+        return self.master, self.exp_avg, self.exp_avg_sq
+
+    def adam_step(self, *, step: int, hyper: dict, rank_grads=None, grad_base: int = 0,
+                  divisor: float = 1.0, reduced_g=None, param16=None, param_base: int = 0,
+                  clip_coef: float = 1.0, grid_blocks: int = 0) -> None:
+        zero_adam_step(chunks_dev=self.chunks_dev, n_chunks=self.chunks.size, begin=self.begin,
+                       end=self.end, master=self.master, exp_avg=self.exp_avg,
+                       exp_avg_sq=self.exp_avg_sq, local_base=self.local_base, step=step,
+                       rank_grads=rank_grads, grad_base=grad_base, divisor=divisor,
+                       reduced_g=reduced_g, param16=param16, param_base=param_base,
+                       clip_coef=clip_coef, grid_blocks=grid_blocks, **hyper)

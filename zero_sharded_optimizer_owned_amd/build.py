@@ -1,0 +1,38 @@
+"""Build libzero_shard.so for gfx950 (hipcc, in place next to this file)."""
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB_PATH = os.path.join(HERE, "libzero_shard.so")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # every fused multiply-add is written explicitly in the kernels
+    "-ffp-contract=off",
+    # IEEE fp32 division and square root, denormals kept (bit-exact reduce)
+    "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
+    # no packed fp32 instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def build(verbose: bool = False) -> str:
+    srcs = [os.path.join(CSRC, "host.cpp"), os.path.join(CSRC, "device.hip")]
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["hipcc", *HIPCC_FLAGS, "-I", INCLUDE, *srcs, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("building libzero_shard.so failed:\n" + " ".join(cmd) + "\n" + res.stderr)
+    os.replace(tmp, LIB_PATH)
+    if verbose:
+        print(" ".join(cmd))
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

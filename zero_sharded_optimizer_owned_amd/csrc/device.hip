@@ -1,0 +1,711 @@
+// Device half of libzero_shard: HIP kernels for gfx950 and the C entry points
+// that validate, plan and launch them.
+//
+// All kernels stream HBM: the step moves ~34-162 bytes per owned parameter for
+// a few dozen fp32 operations, so the design aims at bytes in flight, not at
+// arithmetic.  No MFMA: nothing here is a contraction.
+//   * every stream is read and written as 128-bit vectors of 8 elements
+//     (one vector = 16 B of 16-bit data or 2 x 16 B of fp32); all base
+//     indices are multiples of 8, so the vectors of all streams start at the
+//     same flat indices and only the ends of a range need scalar peels;
+//   * the fused step is a persistent multi-tensor kernel: each 64-lane
+//     wavefront walks the owner's chunk table with a grid stride and
+//     processes whole chunks (no cross-wave synchronisation at all);
+//   * reductions of the squared norm use fp64 per-thread sums, a wavefront
+//     butterfly (DPP/permute shuffles), an LDS stage per block and a second
+//     single-block pass over the per-block partials -- a fixed tree, so the
+//     result is identical run to run;
+//   * the rank sum is one fp32 add per rank in rank order and one IEEE
+//     division (a multiply by 1/divisor when divisor is a power of two,
+//     which gives the same bits), the same instruction sequence on the vector
+//     and peel paths, so every path produces identical bits.
+// Built with -ffp-contract=off: every fused multiply-add below is written
+// explicitly.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "internal.h"
+
+namespace zs {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / 64;
+constexpr int kMaxPartials = 4096;  // per-block partials the check workspace holds
+static_assert(kMaxPartials * (sizeof(double) + sizeof(int32_t)) <= ZERO_CHECK_WS_BYTES,
+              "check workspace too small");
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Element access.  A vector is 8 elements at an index e that is a multiple of
+// 8; `Raw` is its storage as loaded (4 VGPRs for 16-bit data, 8 for fp32), so
+// a batch of loads can be in flight before any of them is widened.
+// ---------------------------------------------------------------------------
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<ZERO_F16> {
+  typedef half8 Raw;
+  static __device__ __forceinline__ Raw load_raw(const void* base, uint64_t e) {
+    return *reinterpret_cast<const half8*>(static_cast<const _Float16*>(base) + e);
+  }
+  static __device__ __forceinline__ float widen(const Raw& h, int k) { return (float)h[k]; }
+  static __device__ __forceinline__ float load1(const void* base, uint64_t e) {
+    return (float)static_cast<const _Float16*>(base)[e];
+  }
+  static __device__ __forceinline__ void store8(void* base, uint64_t e, const float (&x)[8]) {
+    half8 h;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) h[k] = (_Float16)x[k];
+    *reinterpret_cast<half8*>(static_cast<_Float16*>(base) + e) = h;
+  }
+  static __device__ __forceinline__ void store1(void* base, uint64_t e, float x) {
+    static_cast<_Float16*>(base)[e] = (_Float16)x;
+  }
+};
+
+// bfloat16: widening is a 16-bit shift; narrowing rounds to nearest, ties to
+// even, keeps infinities and turns NaN into a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <>
+struct Elem<ZERO_BF16> {
+  typedef uint4 Raw;
+  static __device__ __forceinline__ Raw load_raw(const void* base, uint64_t e) {
+    return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + e);
+  }
+  static __device__ __forceinline__ float widen(const Raw& w, int k) {
+    const uint32_t word = (k >> 1) == 0 ? w.x : (k >> 1) == 1 ? w.y : (k >> 1) == 2 ? w.z : w.w;
+    return __uint_as_float((k & 1) ? (word & 0xFFFF0000u) : (word << 16));
+  }
+  static __device__ __forceinline__ float load1(const void* base, uint64_t e) {
+    return __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[e] << 16);
+  }
+  static __device__ __forceinline__ void store8(void* base, uint64_t e, const float (&x)[8]) {
+    uint4 w;
+    w.x = bf16_bits(x[0]) | (bf16_bits(x[1]) << 16);
+    w.y = bf16_bits(x[2]) | (bf16_bits(x[3]) << 16);
+    w.z = bf16_bits(x[4]) | (bf16_bits(x[5]) << 16);
+    w.w = bf16_bits(x[6]) | (bf16_bits(x[7]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + e) = w;
+  }
+  static __device__ __forceinline__ void store1(void* base, uint64_t e, float x) {
+    static_cast<uint16_t*>(base)[e] = (uint16_t)bf16_bits(x);
+  }
+};
+
+struct F32x8 {
+  float4v lo, hi;
+};
+
+template <>
+struct Elem<ZERO_F32> {
+  typedef F32x8 Raw;
+  static __device__ __forceinline__ Raw load_raw(const void* base, uint64_t e) {
+    const float4v* p = reinterpret_cast<const float4v*>(static_cast<const float*>(base) + e);
+    return F32x8{p[0], p[1]};
+  }
+  static __device__ __forceinline__ float widen(const Raw& r, int k) {
+    return k < 4 ? r.lo[k] : r.hi[k - 4];
+  }
+  static __device__ __forceinline__ float load1(const void* base, uint64_t e) {
+    return static_cast<const float*>(base)[e];
+  }
+  static __device__ __forceinline__ void store8(void* base, uint64_t e, const float (&x)[8]) {
+    float4v* p = reinterpret_cast<float4v*>(static_cast<float*>(base) + e);
+    p[0] = float4v{x[0], x[1], x[2], x[3]};
+    p[1] = float4v{x[4], x[5], x[6], x[7]};
+  }
+  static __device__ __forceinline__ void store1(void* base, uint64_t e, float x) {
+    static_cast<float*>(base)[e] = x;
+  }
+};
+
+// fp32 vector load into registers.
+__device__ __forceinline__ void load8f(const float* base, uint64_t e, float (&x)[8]) {
+  const F32x8 r = Elem<ZERO_F32>::load_raw(base, e);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) x[k] = Elem<ZERO_F32>::widen(r, k);
+}
+
+// ---------------------------------------------------------------------------
+// The rank reduce: s = start; s += g_r in rank order (fp32); s / divisor.
+// ---------------------------------------------------------------------------
+struct RankSet {
+  const void* ptr[ZERO_MAX_RANKS];
+  uint32_t R;
+  uint64_t base;       // flat index of element 0 of every rank buffer
+  float divisor;
+  float inv_divisor;   // exact reciprocal when divisor is a power of two
+  int32_t div_pow2;
+};
+
+__device__ __forceinline__ float divide(float s, const RankSet& rs) {
+  // x * 2^-k and x / 2^k are the same real number, so both round identically.
+  return rs.div_pow2 ? s * rs.inv_divisor : s / rs.divisor;
+}
+
+// Batch of ranks whose loads are issued together before their adds.
+template <int DT>
+struct RankBatch {
+  static constexpr int value = DT == ZERO_F32 ? 4 : 8;  // 32 VGPRs of raw data per vector
+};
+
+template <int DT, int U>
+__device__ __forceinline__ void reduce_vec(const RankSet& rs, const uint64_t (&f)[U],
+                                           float (&s)[U][8]) {
+  constexpr int B = RankBatch<DT>::value;
+  typedef typename Elem<DT>::Raw Raw;
+  for (uint32_t r0 = 0; r0 < rs.R; r0 += B) {
+    Raw x[B][U];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      if (r0 + j < rs.R) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[j][u] = Elem<DT>::load_raw(rs.ptr[r0 + j], f[u] - rs.base);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      if (r0 + j < rs.R) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) s[u][k] = s[u][k] + Elem<DT>::widen(x[j][u], k);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s[u][k] = divide(s[u][k], rs);
+}
+
+template <int DT>
+__device__ __forceinline__ float reduce_one(const RankSet& rs, uint64_t f, float start) {
+  float s = start;
+  for (uint32_t r = 0; r < rs.R; ++r) s = s + Elem<DT>::load1(rs.ptr[r], f - rs.base);
+  return divide(s, rs);
+}
+
+// ---------------------------------------------------------------------------
+// Squared-norm / overflow reduction: wave butterfly, LDS across waves.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = x + __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Block-wide (sum, any) with a fixed order; the result is valid in thread 0.
+__device__ __forceinline__ void block_reduce(double& sq, int& bad) {
+  __shared__ double s_sum[kWavesPerBlock];
+  __shared__ int s_bad[kWavesPerBlock];
+  sq = wave_sum(sq);
+  const int any = __any(bad);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s_sum[w] = sq;
+    s_bad[w] = any;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = s_sum[0];
+    int b = s_bad[0];
+    for (int i = 1; i < kWavesPerBlock; ++i) {
+      t = t + s_sum[i];
+      b |= s_bad[i];
+    }
+    sq = t;
+    bad = b;
+  }
+}
+
+__device__ __forceinline__ void check_accum(float g, double& sq, int& bad) {
+  const double d = (double)g;
+  sq = fma(d, d, sq);  // d*d is exact in fp64, so the fma rounds only the sum
+  bad |= !__builtin_isfinite(g);
+}
+
+struct CheckOut {
+  double* partial;  // [gridDim.x]
+  int32_t* flags;   // [gridDim.x]
+};
+
+// ---------------------------------------------------------------------------
+// K1: owner reduce over a contiguous flat range, optional fused check.
+// ---------------------------------------------------------------------------
+struct ReduceArgs {
+  RankSet rs;
+  uint64_t begin, end;
+  float* out;
+  uint64_t out_base;
+  CheckOut chk;
+};
+
+template <int DT, bool ACCUM, bool CHECK>
+__global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs a) {
+  const uint64_t f0 = a.begin, f1 = a.end;
+  const uint64_t a0 = min(f1, (f0 + 7) & ~7ull);
+  const uint64_t a1 = max(a0, f1 & ~7ull);
+  double sq = 0.0;
+  int bad = 0;
+  if (blockIdx.x == 0) {
+    const uint64_t t = threadIdx.x;
+    uint64_t f = ~0ull;
+    if (t < a0 - f0) f = f0 + t;
+    else if (t >= 8 && t - 8 < f1 - a1) f = a1 + (t - 8);
+    if (f != ~0ull) {
+      const float start = ACCUM ? a.out[f - a.out_base] : 0.0f;
+      const float g = reduce_one<DT>(a.rs, f, start);
+      a.out[f - a.out_base] = g;
+      if (CHECK) check_accum(g, sq, bad);
+    }
+  }
+  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
+  for (uint64_t v = a0 / 8 + (uint64_t)blockIdx.x * kBlock + threadIdx.x; v < a1 / 8; v += stride) {
+    const uint64_t f[1] = {v * 8};
+    float s[1][8];
+    if (ACCUM) {
+      load8f(a.out, f[0] - a.out_base, s[0]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s[0][k] = 0.0f;
+    }
+    reduce_vec<DT, 1>(a.rs, f, s);
+    Elem<ZERO_F32>::store8(a.out, f[0] - a.out_base, s[0]);
+    if (CHECK) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) check_accum(s[0][k], sq, bad);
+    }
+  }
+  if (CHECK) {
+    block_reduce(sq, bad);
+    if (threadIdx.x == 0) {
+      a.chk.partial[blockIdx.x] = sq;
+      a.chk.flags[blockIdx.x] = bad;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K2: check of a stored fp32 gradient (first stage), and the final stage.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kBlock) check_kernel(const float* g, uint64_t n, CheckOut chk) {
+  const uint64_t a1 = n & ~7ull;
+  double sq = 0.0;
+  int bad = 0;
+  if (blockIdx.x == 0 && threadIdx.x < n - a1) check_accum(g[a1 + threadIdx.x], sq, bad);
+  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
+  for (uint64_t v = (uint64_t)blockIdx.x * kBlock + threadIdx.x; v < a1 / 8; v += stride) {
+    float x[8];
+    load8f(g, v * 8, x);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) check_accum(x[k], sq, bad);
+  }
+  block_reduce(sq, bad);
+  if (threadIdx.x == 0) {
+    chk.partial[blockIdx.x] = sq;
+    chk.flags[blockIdx.x] = bad;
+  }
+}
+
+__global__ void __launch_bounds__(kBlock) check_final_kernel(CheckOut chk, uint32_t parts,
+                                                             int32_t* d_overflow, double* d_sumsq) {
+  double sq = 0.0;
+  int bad = 0;
+  for (uint32_t i = threadIdx.x; i < parts; i += kBlock) {
+    sq = sq + chk.partial[i];
+    bad |= chk.flags[i];
+  }
+  block_reduce(sq, bad);
+  if (threadIdx.x == 0) {
+    *d_sumsq = sq;
+    *d_overflow = bad ? 1 : 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K3/K4: fused owner step over the chunk table.
+// ---------------------------------------------------------------------------
+struct AdamConst {
+  float beta1, one_minus_beta1, beta2, one_minus_beta2;
+  float step_size;     // lr / (1 - beta1^t)
+  float inv_sqrt_bc2;  // 1 / sqrt(1 - beta2^t)
+  float eps;
+  float decay;  // 1 - lr * wd for AdamW, else 1
+  float l2;     // wd for classic Adam, else 0
+  float clip;
+};
+
+__device__ __forceinline__ void adam_update(float g, float& w, float& m, float& v,
+                                            const AdamConst& c) {
+  float gc = g * c.clip;
+  if (c.l2 != 0.0f) gc = fmaf(c.l2, w, gc);
+  m = fmaf(c.beta1, m, c.one_minus_beta1 * gc);
+  v = fmaf(c.beta2, v, (c.one_minus_beta2 * gc) * gc);
+  const float denom = fmaf(__builtin_sqrtf(v), c.inv_sqrt_bc2, c.eps);
+  const float upd = m / denom;
+  w = fmaf(-c.step_size, upd, w * c.decay);
+}
+
+struct AdamArgs {
+  RankSet rs;
+  const zero_chunk* chunks;
+  uint64_t n_chunks;
+  uint64_t begin, end;
+  const float* reduced_g;
+  float *w, *m, *v;
+  uint64_t local_base;
+  void* p16;
+  uint64_t param_base;
+  AdamConst c;
+};
+
+template <int GDT, int PDT, bool REDUCED, int U>
+__device__ __forceinline__ void adam_vec(const AdamArgs& a, const uint64_t (&f)[U]) {
+  float g[U][8];
+  if (REDUCED) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) load8f(a.reduced_g, f[u] - a.local_base, g[u]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) g[u][k] = 0.0f;
+    reduce_vec<GDT, U>(a.rs, f, g);
+  }
+  float w[U][8], m[U][8], v[U][8];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    load8f(a.w, f[u] - a.local_base, w[u]);
+    load8f(a.m, f[u] - a.local_base, m[u]);
+    load8f(a.v, f[u] - a.local_base, v[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) adam_update(g[u][k], w[u][k], m[u][k], v[u][k], a.c);
+    Elem<ZERO_F32>::store8(a.w, f[u] - a.local_base, w[u]);
+    Elem<ZERO_F32>::store8(a.m, f[u] - a.local_base, m[u]);
+    Elem<ZERO_F32>::store8(a.v, f[u] - a.local_base, v[u]);
+    if constexpr (PDT != ZERO_NONE) Elem<PDT>::store8(a.p16, f[u] - a.param_base, w[u]);
+  }
+}
+
+template <int GDT, int PDT, bool REDUCED>
+__device__ __forceinline__ void adam_one(const AdamArgs& a, uint64_t f) {
+  const float g = REDUCED ? a.reduced_g[f - a.local_base] : reduce_one<GDT>(a.rs, f, 0.0f);
+  const uint64_t l = f - a.local_base;
+  float w = a.w[l], m = a.m[l], v = a.v[l];
+  adam_update(g, w, m, v, a.c);
+  a.w[l] = w;
+  a.m[l] = m;
+  a.v[l] = v;
+  if constexpr (PDT != ZERO_NONE) Elem<PDT>::store1(a.p16, f - a.param_base, w);
+}
+
+template <int GDT, int PDT, bool REDUCED>
+__global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs a) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint64_t wave =
+      __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const uint64_t n_waves = (uint64_t)gridDim.x * kWavesPerBlock;
+  for (uint64_t c = wave; c < a.n_chunks; c += n_waves) {
+    const zero_chunk ch = a.chunks[c];
+    const uint64_t f0 = max(ch.flat, a.begin);
+    const uint64_t f1 = min(ch.flat + ch.len, a.end);
+    if (f0 >= f1) continue;
+    const uint64_t a0 = min(f1, (f0 + 7) & ~7ull);
+    const uint64_t a1 = max(a0, f1 & ~7ull);
+    // Scalar peels: lanes 0-6 take the head before the first vector boundary,
+    // lanes 8-14 the tail after the last one.
+    if (lane < a0 - f0) adam_one<GDT, PDT, REDUCED>(a, f0 + lane);
+    else if (lane >= 8 && lane - 8 < f1 - a1) adam_one<GDT, PDT, REDUCED>(a, a1 + lane - 8);
+    uint64_t vi = a0 / 8 + lane;
+    const uint64_t vend = a1 / 8;
+    for (; vi + 64 < vend; vi += 128) {
+      const uint64_t f[2] = {vi * 8, (vi + 64) * 8};
+      adam_vec<GDT, PDT, REDUCED, 2>(a, f);
+    }
+    if (vi < vend) {
+      const uint64_t f[1] = {vi * 8};
+      adam_vec<GDT, PDT, REDUCED, 1>(a, f);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side planning and validation.
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];  // 0 = not yet queried
+
+int cu_count(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(ZERO_EHIP, "hipGetDevice failed");
+  if (dev >= 0 && dev < kMaxDevices && __atomic_load_n(&g_cu_count[dev], __ATOMIC_RELAXED) > 0) {
+    *out = __atomic_load_n(&g_cu_count[dev], __ATOMIC_RELAXED);
+    return ZERO_OK;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return fail(ZERO_EHIP, "querying the compute-unit count failed");
+  if (dev >= 0 && dev < kMaxDevices) __atomic_store_n(&g_cu_count[dev], cus, __ATOMIC_RELAXED);
+  *out = cus;
+  return ZERO_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_pow2_float(float d, float* inv) {
+  int e = 0;
+  const float mant = std::frexp(d, &e);
+  if (mant != 0.5f) return false;
+  const float r = std::ldexp(1.0f, 1 - e);  // 1/d exactly
+  if (!std::isfinite(r) || r == 0.0f || std::fpclassify(r) == FP_SUBNORMAL) return false;
+  *inv = r;
+  return true;
+}
+
+int fill_ranks(RankSet* rs, const void* const* rank_grads, uint32_t R, int dtype, uint64_t base,
+               uint64_t begin, float divisor, const char* who) {
+  if (R == 0 || R > ZERO_MAX_RANKS)
+    return fail(ZERO_EINVAL, "%s: R = %u outside [1, %d]", who, R, ZERO_MAX_RANKS);
+  if (!rank_grads) return fail(ZERO_EINVAL, "%s: rank_grads is NULL", who);
+  if (dtype != ZERO_F16 && dtype != ZERO_BF16 && dtype != ZERO_F32)
+    return fail(ZERO_EINVAL, "%s: unknown gradient dtype %d", who, dtype);
+  if (base % 8 != 0) return fail(ZERO_EINVAL, "%s: grad_base must be a multiple of 8", who);
+  if (begin < base) return fail(ZERO_EINVAL, "%s: begin lies below grad_base", who);
+  if (!(divisor > 0.0f) || !std::isfinite(divisor))
+    return fail(ZERO_EINVAL, "%s: divisor must be finite and > 0", who);
+  for (uint32_t r = 0; r < R; ++r) {
+    if (!rank_grads[r]) return fail(ZERO_EINVAL, "%s: rank buffer %u is NULL", who, r);
+    if (!aligned16(rank_grads[r]))
+      return fail(ZERO_EINVAL, "%s: rank buffer %u is not 16-byte aligned", who, r);
+    rs->ptr[r] = rank_grads[r];
+  }
+  for (uint32_t r = R; r < ZERO_MAX_RANKS; ++r) rs->ptr[r] = nullptr;
+  rs->R = R;
+  rs->base = base;
+  rs->divisor = divisor;
+  float inv = 0.0f;
+  rs->div_pow2 = is_pow2_float(divisor, &inv) ? 1 : 0;
+  rs->inv_divisor = inv;
+  return ZERO_OK;
+}
+
+int check_workspace(void* ws, size_t ws_bytes, const char* who) {
+  if (!ws) return fail(ZERO_EINVAL, "%s: workspace is NULL", who);
+  if (ws_bytes < ZERO_CHECK_WS_BYTES)
+    return fail(ZERO_EINVAL, "%s: workspace needs %d bytes, got %zu", who, ZERO_CHECK_WS_BYTES,
+                ws_bytes);
+  if (reinterpret_cast<uintptr_t>(ws) & 255u)
+    return fail(ZERO_EINVAL, "%s: workspace must be 256-byte aligned", who);
+  return ZERO_OK;
+}
+
+CheckOut check_layout(void* ws) {
+  CheckOut c;
+  c.partial = static_cast<double*>(ws);
+  c.flags = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + kMaxPartials * sizeof(double));
+  return c;
+}
+
+uint32_t stream_grid(uint64_t n_vectors, int cus, uint32_t cap) {
+  uint64_t want = (n_vectors + kBlock - 1) / kBlock;
+  const uint64_t full = (uint64_t)cus * 8;  // eight 256-thread blocks per CU
+  if (want > full) want = full;
+  if (want > cap) want = cap;
+  return want == 0 ? 1u : (uint32_t)want;
+}
+
+int launch_status(const char* who) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
+  return ZERO_OK;
+}
+
+template <int DT>
+void launch_reduce(const ReduceArgs& a, bool accum, bool check, uint32_t grid, hipStream_t s) {
+  if (accum) {
+    if (check) hipLaunchKernelGGL((reduce_kernel<DT, true, true>), grid, kBlock, 0, s, a);
+    else hipLaunchKernelGGL((reduce_kernel<DT, true, false>), grid, kBlock, 0, s, a);
+  } else {
+    if (check) hipLaunchKernelGGL((reduce_kernel<DT, false, true>), grid, kBlock, 0, s, a);
+    else hipLaunchKernelGGL((reduce_kernel<DT, false, false>), grid, kBlock, 0, s, a);
+  }
+}
+
+template <int GDT, bool REDUCED>
+void launch_adam_p(const AdamArgs& a, int pdt, uint32_t grid, hipStream_t s) {
+  if (pdt == ZERO_F16) hipLaunchKernelGGL((adam_kernel<GDT, ZERO_F16, REDUCED>), grid, kBlock, 0, s, a);
+  else if (pdt == ZERO_BF16) hipLaunchKernelGGL((adam_kernel<GDT, ZERO_BF16, REDUCED>), grid, kBlock, 0, s, a);
+  else hipLaunchKernelGGL((adam_kernel<GDT, ZERO_NONE, REDUCED>), grid, kBlock, 0, s, a);
+}
+
+}  // namespace
+}  // namespace zs
+
+using namespace zs;
+
+extern "C" int zero_reduce_owned(const void* const* rank_grads, uint32_t R, int grad_dtype,
+                                 uint64_t grad_base, uint64_t begin, uint64_t n, float divisor,
+                                 int accumulate, float* out, uint64_t out_base,
+                                 int32_t* d_overflow, double* d_sumsq, void* workspace,
+                                 size_t ws_bytes, hipStream_t stream) {
+  static const char* who = "zero_reduce_owned";
+  clear_error();
+  ReduceArgs a;
+  std::memset(&a, 0, sizeof a);
+  int rc = fill_ranks(&a.rs, rank_grads, R, grad_dtype, grad_base, begin, divisor, who);
+  if (rc) return rc;
+  if (!out) return fail(ZERO_EINVAL, "%s: out is NULL", who);
+  if (!aligned16(out)) return fail(ZERO_EINVAL, "%s: out is not 16-byte aligned", who);
+  if (out_base % 8 != 0) return fail(ZERO_EINVAL, "%s: out_base must be a multiple of 8", who);
+  if (begin < out_base) return fail(ZERO_EINVAL, "%s: begin lies below out_base", who);
+  if (n > UINT64_MAX - begin) return fail(ZERO_EINVAL, "%s: begin + n overflows", who);
+  const bool check = d_overflow != nullptr || d_sumsq != nullptr;
+  if (check) {
+    if (!d_overflow || !d_sumsq)
+      return fail(ZERO_EINVAL, "%s: give both d_overflow and d_sumsq, or neither", who);
+    if ((rc = check_workspace(workspace, ws_bytes, who))) return rc;
+  }
+  if (n == 0) return ZERO_OK;
+  int cus = 0;
+  if ((rc = cu_count(&cus))) return rc;
+  a.begin = begin;
+  a.end = begin + n;
+  a.out = out;
+  a.out_base = out_base;
+  if (check) a.chk = check_layout(workspace);
+  const uint32_t grid = stream_grid((n + 7) / 8, cus, kMaxPartials);
+  switch (grad_dtype) {
+    case ZERO_F16: launch_reduce<ZERO_F16>(a, accumulate != 0, check, grid, stream); break;
+    case ZERO_BF16: launch_reduce<ZERO_BF16>(a, accumulate != 0, check, grid, stream); break;
+    default: launch_reduce<ZERO_F32>(a, accumulate != 0, check, grid, stream); break;
+  }
+  if ((rc = launch_status(who))) return rc;
+  if (check) {
+    hipLaunchKernelGGL(check_final_kernel, 1, kBlock, 0, stream, a.chk, grid, d_overflow, d_sumsq);
+    if ((rc = launch_status(who))) return rc;
+  }
+  return ZERO_OK;
+}
+
+extern "C" int zero_grad_check(const float* g, uint64_t n, int32_t* d_overflow, double* d_sumsq,
+                               void* workspace, size_t ws_bytes, hipStream_t stream) {
+  static const char* who = "zero_grad_check";
+  clear_error();
+  if (!d_overflow || !d_sumsq) return fail(ZERO_EINVAL, "%s: NULL output", who);
+  int rc = check_workspace(workspace, ws_bytes, who);
+  if (rc) return rc;
+  if (n > 0 && !g) return fail(ZERO_EINVAL, "%s: g is NULL", who);
+  if (n > 0 && !aligned16(g)) return fail(ZERO_EINVAL, "%s: g is not 16-byte aligned", who);
+  int cus = 0;
+  if ((rc = cu_count(&cus))) return rc;
+  const uint32_t grid = stream_grid(n / 8, cus, kMaxPartials);
+  const CheckOut chk = check_layout(workspace);
+  hipLaunchKernelGGL(check_kernel, grid, kBlock, 0, stream, g, n, chk);
+  if ((rc = launch_status(who))) return rc;
+  hipLaunchKernelGGL(check_final_kernel, 1, kBlock, 0, stream, chk, grid, d_overflow, d_sumsq);
+  return launch_status(who);
+}
+
+extern "C" int zero_adam_step(const zero_adam_args* p, hipStream_t stream) {
+  static const char* who = "zero_adam_step";
+  clear_error();
+  if (!p) return fail(ZERO_EINVAL, "%s: args is NULL", who);
+  AdamArgs a;
+  std::memset(&a, 0, sizeof a);
+  int rc;
+  if (p->step == 0) return fail(ZERO_EINVAL, "%s: step counts from 1", who);
+  if (p->begin > p->end) return fail(ZERO_EINVAL, "%s: begin > end", who);
+  if (p->n_chunks > 0 && !p->chunks) return fail(ZERO_EINVAL, "%s: chunks is NULL", who);
+  const bool reduced = p->reduced_g != nullptr;
+  if (reduced) {
+    if (!aligned16(p->reduced_g))
+      return fail(ZERO_EINVAL, "%s: reduced_g is not 16-byte aligned", who);
+  } else if ((rc = fill_ranks(&a.rs, p->rank_grads, p->R, p->grad_dtype, p->grad_base, p->begin,
+                              p->divisor, who))) {
+    return rc;
+  }
+  if (!p->master || !p->exp_avg || !p->exp_avg_sq)
+    return fail(ZERO_EINVAL, "%s: master/exp_avg/exp_avg_sq must be given", who);
+  if (!aligned16(p->master) || !aligned16(p->exp_avg) || !aligned16(p->exp_avg_sq))
+    return fail(ZERO_EINVAL, "%s: state arrays must be 16-byte aligned", who);
+  if (p->local_base % 8 != 0 || p->local_base > p->begin)
+    return fail(ZERO_EINVAL, "%s: local_base must be a multiple of 8 and <= begin", who);
+  const int pdt = p->param_dtype;
+  if (pdt != ZERO_NONE && pdt != ZERO_F16 && pdt != ZERO_BF16)
+    return fail(ZERO_EINVAL, "%s: param_dtype must be NONE, F16 or BF16", who);
+  if (pdt != ZERO_NONE) {
+    if (!p->param16) return fail(ZERO_EINVAL, "%s: param16 is NULL", who);
+    if (!aligned16(p->param16)) return fail(ZERO_EINVAL, "%s: param16 is not 16-byte aligned", who);
+    if (p->param_base % 8 != 0 || p->param_base > p->begin)
+      return fail(ZERO_EINVAL, "%s: param_base must be a multiple of 8 and <= begin", who);
+  }
+  const double hp[] = {p->lr, p->beta1, p->beta2, p->eps, p->weight_decay, p->clip_coef};
+  for (double x : hp)
+    if (!std::isfinite(x)) return fail(ZERO_EINVAL, "%s: non-finite hyperparameter", who);
+  if (p->lr < 0 || p->eps < 0 || p->weight_decay < 0 || p->clip_coef < 0)
+    return fail(ZERO_EINVAL, "%s: lr, eps, weight_decay and clip_coef must be >= 0", who);
+  if (p->beta1 < 0 || p->beta1 >= 1 || p->beta2 < 0 || p->beta2 >= 1)
+    return fail(ZERO_EINVAL, "%s: betas must lie in [0, 1)", who);
+  if (p->n_chunks == 0 || p->begin == p->end) return ZERO_OK;
+  int cus = 0;
+  if ((rc = cu_count(&cus))) return rc;
+
+  // Constants in fp64, each rounded once to fp32.
+  const double t = (double)p->step;
+  const double bc1 = 1.0 - std::pow(p->beta1, t);
+  const double bc2 = 1.0 - std::pow(p->beta2, t);
+  a.c.beta1 = (float)p->beta1;
+  a.c.one_minus_beta1 = (float)(1.0 - p->beta1);
+  a.c.beta2 = (float)p->beta2;
+  a.c.one_minus_beta2 = (float)(1.0 - p->beta2);
+  a.c.step_size = (float)(p->lr / bc1);
+  a.c.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+  a.c.eps = (float)p->eps;
+  a.c.decay = p->adamw ? (float)(1.0 - p->lr * p->weight_decay) : 1.0f;
+  a.c.l2 = p->adamw ? 0.0f : (float)p->weight_decay;
+  a.c.clip = (float)p->clip_coef;
+  a.chunks = p->chunks;
+  a.n_chunks = p->n_chunks;
+  a.begin = p->begin;
+  a.end = p->end;
+  a.reduced_g = p->reduced_g;
+  a.w = p->master;
+  a.m = p->exp_avg;
+  a.v = p->exp_avg_sq;
+  a.local_base = p->local_base;
+  a.p16 = pdt != ZERO_NONE ? p->param16 : nullptr;
+  a.param_base = p->param_base;
+
+  uint32_t grid = p->grid_blocks;
+  if (grid == 0) {
+    const uint64_t by_chunks = (p->n_chunks + kWavesPerBlock - 1) / kWavesPerBlock;
+    const uint64_t full = (uint64_t)cus * 8;
+    grid = (uint32_t)(by_chunks < full ? by_chunks : full);
+  }
+  if (reduced) {
+    launch_adam_p<ZERO_F32, true>(a, pdt, grid, stream);
+  } else {
+    switch (p->grad_dtype) {
+      case ZERO_F16: launch_adam_p<ZERO_F16, false>(a, pdt, grid, stream); break;
+      case ZERO_BF16: launch_adam_p<ZERO_BF16, false>(a, pdt, grid, stream); break;
+      default: launch_adam_p<ZERO_F32, false>(a, pdt, grid, stream); break;
+    }
+  }
+  return launch_status(who);
+}

@@ -1,0 +1,174 @@
+// Host half of libzero_shard: layout, chunk table, state accounting, clip
+// scalar and the thread-local error message.  No device code here.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "internal.h"
+
+namespace zs {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+}  // namespace zs
+
+using zs::fail;
+using u128 = unsigned __int128;
+
+extern "C" const char* zero_last_error(void) { return zs::g_last_error.c_str(); }
+
+// Owner ranges over the padded total P: [floor(P r / R), floor(P (r+1) / R)).
+// ([Deep dive] "Reduce first, then update the owned slice", contiguous
+// ownership; the products are taken in 128 bits.)
+extern "C" int zero_shard_layout(const uint64_t* numel, uint32_t n_tensors, uint32_t ranks,
+                                 uint32_t align_elems, uint64_t* tensor_offset,
+                                 uint64_t* padded_total, uint64_t* owner_begin,
+                                 uint64_t* owner_end) {
+  zs::clear_error();
+  if (!numel || !tensor_offset || !padded_total || !owner_begin || !owner_end)
+    return fail(ZERO_EINVAL, "zero_shard_layout: NULL pointer argument");
+  if (n_tensors == 0) return fail(ZERO_EINVAL, "zero_shard_layout: no tensors");
+  if (ranks == 0) return fail(ZERO_EINVAL, "zero_shard_layout: ranks must be >= 1");
+  if (align_elems == 0) return fail(ZERO_EINVAL, "zero_shard_layout: alignment must be >= 1");
+  u128 total = 0;
+  for (uint32_t k = 0; k < n_tensors; ++k) {
+    if (numel[k] == 0) return fail(ZERO_EINVAL, "zero_shard_layout: tensor %u has 0 elements", k);
+    const u128 padded = ((u128)numel[k] + align_elems - 1) / align_elems * align_elems;
+    if (total + padded > (u128)UINT64_MAX)
+      return fail(ZERO_ERANGE, "zero_shard_layout: padded total exceeds 64 bits");
+    total += padded;
+  }
+  // All checks passed: write outputs.
+  u128 off = 0;
+  for (uint32_t k = 0; k < n_tensors; ++k) {
+    tensor_offset[k] = (uint64_t)off;
+    off += ((u128)numel[k] + align_elems - 1) / align_elems * align_elems;
+  }
+  *padded_total = (uint64_t)total;
+  for (uint32_t r = 0; r < ranks; ++r) {
+    owner_begin[r] = (uint64_t)(total * r / ranks);
+    owner_end[r] = (uint64_t)(total * (r + 1) / ranks);
+  }
+  return ZERO_OK;
+}
+
+extern "C" int zero_chunk_table(const uint64_t* numel, const uint64_t* tensor_offset,
+                                uint32_t n_tensors, uint64_t begin, uint64_t end,
+                                uint32_t max_chunk_elems, zero_chunk* out, uint64_t capacity,
+                                uint64_t* n_chunks) {
+  zs::clear_error();
+  if (!n_chunks) return fail(ZERO_EINVAL, "zero_chunk_table: n_chunks is NULL");
+  if (n_tensors > 0 && (!numel || !tensor_offset))
+    return fail(ZERO_EINVAL, "zero_chunk_table: NULL tensor arrays");
+  if (begin > end) return fail(ZERO_EINVAL, "zero_chunk_table: begin > end");
+  if (max_chunk_elems < 8 || max_chunk_elems % 8 != 0)
+    return fail(ZERO_EINVAL, "zero_chunk_table: max_chunk_elems must be a positive multiple of 8");
+  if (capacity > 0 && !out) return fail(ZERO_EINVAL, "zero_chunk_table: out is NULL");
+  for (uint32_t k = 0; k < n_tensors; ++k) {
+    if (numel[k] == 0) return fail(ZERO_EINVAL, "zero_chunk_table: tensor %u has 0 elements", k);
+    if ((u128)tensor_offset[k] + numel[k] > (u128)UINT64_MAX)
+      return fail(ZERO_EINVAL, "zero_chunk_table: tensor %u extends past 2^64", k);
+    if (k > 0 && tensor_offset[k] < tensor_offset[k - 1] + numel[k - 1])
+      return fail(ZERO_EINVAL, "zero_chunk_table: tensor %u overlaps or precedes tensor %u", k,
+                  k - 1);
+  }
+  const uint64_t C = max_chunk_elems;
+  uint64_t count = 0;
+  for (uint32_t k = 0; k < n_tensors; ++k) {
+    const uint64_t t0 = tensor_offset[k], t1 = tensor_offset[k] + numel[k];
+    uint64_t b = t0 > begin ? t0 : begin;
+    const uint64_t e = t1 < end ? t1 : end;
+    while (b < e) {
+      const uint64_t cut = (b / C + 1) * C;  // next multiple of C after b
+      const uint64_t stop = cut < e ? cut : e;
+      if (out && count < capacity) {
+        out[count].flat = b;
+        out[count].len = (uint32_t)(stop - b);
+        out[count].tensor = k;
+      }
+      ++count;
+      b = stop;
+    }
+  }
+  *n_chunks = count;
+  if (out == nullptr && capacity == 0) return ZERO_OK;
+  if (count > capacity)
+    return fail(ZERO_ERANGE, "zero_chunk_table: %llu chunks needed, capacity %llu",
+                (unsigned long long)count, (unsigned long long)capacity);
+  return ZERO_OK;
+}
+
+namespace {
+// whole + shared / R as a reduced fraction; whole and shared are exact
+// products of 64-bit by 32-bit values (at most 2^98), R < 2^64.
+int make_ratio(u128 whole, u128 shared, uint64_t R, zero_ratio* out) {
+  // Reduce shared / R first so that whole * den stays within 128 bits.
+  u128 a = shared, b = R;
+  while (b) {
+    const u128 t = a % b;
+    a = b;
+    b = t;
+  }
+  const u128 g = shared == 0 ? (u128)R : a;
+  const u128 sn = shared / g, den = (u128)R / g;
+  if (whole > (u128)UINT64_MAX || den > (u128)UINT64_MAX) return ZERO_ERANGE;
+  const u128 num = whole * den + sn;  // < 2^64 * 2^64: fits
+  if (num > (u128)UINT64_MAX) return ZERO_ERANGE;
+  out->num = (uint64_t)num;
+  out->den = (uint64_t)den;
+  return ZERO_OK;
+}
+}  // namespace
+
+// [Deep dive] "Count state before choosing a stage"; [ZeRO Q&A] "Memory
+// Footprint Reduction Matrix".
+extern "C" int zero_state_bytes(uint64_t params, uint64_t ranks, uint32_t param_bytes,
+                                uint32_t grad_bytes, uint32_t optim_bytes, zero_ratio out[4]) {
+  zs::clear_error();
+  if (!out) return fail(ZERO_EINVAL, "zero_state_bytes: out is NULL");
+  if (params == 0 || ranks == 0 || param_bytes == 0 || grad_bytes == 0 || optim_bytes == 0)
+    return fail(ZERO_EINVAL, "zero_state_bytes: counts and byte widths must be positive");
+  const u128 P = params, p = param_bytes, g = grad_bytes, o = optim_bytes;
+  zero_ratio tmp[4];
+  const u128 parts[4][2] = {
+      {P * (p + g + o), 0},  // DP
+      {P * (p + g), P * o},  // ZeRO-1
+      {P * p, P * (g + o)},  // ZeRO-2
+      {0, P * (p + g + o)},  // ZeRO-3
+  };
+  for (int s = 0; s < 4; ++s) {
+    if (make_ratio(parts[s][0], parts[s][1], ranks, &tmp[s]) != ZERO_OK)
+      return fail(ZERO_ERANGE, "zero_state_bytes: result exceeds 64 bits");
+  }
+  std::memcpy(out, tmp, sizeof tmp);
+  return ZERO_OK;
+}
+
+extern "C" int zero_clip_coef(double sumsq, double max_norm, double eps, float* coef) {
+  zs::clear_error();
+  if (!coef) return fail(ZERO_EINVAL, "zero_clip_coef: coef is NULL");
+  if (!std::isfinite(sumsq) || sumsq < 0.0)
+    return fail(ZERO_EINVAL, "zero_clip_coef: sumsq must be finite and >= 0");
+  if (!std::isfinite(max_norm) || max_norm <= 0.0)
+    return fail(ZERO_EINVAL, "zero_clip_coef: max_norm must be finite and > 0");
+  if (!std::isfinite(eps) || eps < 0.0)
+    return fail(ZERO_EINVAL, "zero_clip_coef: eps must be finite and >= 0");
+  const double c = max_norm / (std::sqrt(sumsq) + eps);
+  *coef = (float)(c < 1.0 ? c : 1.0);
+  return ZERO_OK;
+}
