@@ -206,20 +206,50 @@ def hyper(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, adamw=Tru
     return Hyper(lr, beta1, beta2, eps, weight_decay, 1 if adamw else 0, step, clip_coef)
 
 
-def build() -> str:
+GCC_FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
+             "-shared", "-Wall"]
+
+
+def build(src: str = None, out: str = None) -> str:
     """Compile zero_oracle.c with gcc into liboracle.so (no fast-math, no FMA contraction)."""
-    src = os.path.join(_HERE, "zero_oracle.c")
-    tmp = LIB_PATH + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
-           "-shared", "-Wall", src, "-o", tmp, "-lm"]
+    src = src or os.path.join(_HERE, "zero_oracle.c")
+    out = out or LIB_PATH
+    tmp = out + ".tmp"
+    cmd = ["gcc", *GCC_FLAGS, src, "-o", tmp, "-lm"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("building the oracle failed:\n" + res.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 _lib = None
+
+
+def load(path: str):
+    """Open a build of zero_oracle.c and declare its signatures."""
+    L = ct.CDLL(path)
+    P, U64, F, D, I = ct.c_void_p, ct.c_uint64, ct.c_float, ct.c_double, ct.c_int
+    L.oracle_f32_to_f16.restype = ct.c_uint16
+    L.oracle_f32_to_f16.argtypes = [F]
+    L.oracle_f32_to_bf16.restype = ct.c_uint16
+    L.oracle_f32_to_bf16.argtypes = [F]
+    L.oracle_f16_value.restype = D
+    L.oracle_f16_value.argtypes = [ct.c_uint16]
+    L.oracle_bf16_value.restype = D
+    L.oracle_bf16_value.argtypes = [ct.c_uint16]
+    L.oracle_encode16.argtypes = [P, U64, I, P]
+    L.oracle_reduce.argtypes = [ct.c_uint32, I, P, U64, F, I, P]
+    L.oracle_accumulate.argtypes = [I, P, U64, I, P]
+    L.oracle_grad_check.argtypes = [P, U64, P, P]
+    L.oracle_clip_coef.restype = D
+    L.oracle_clip_coef.argtypes = [D, D, D]
+    L.oracle_adam_f64.argtypes = [U64, P, P, P, P, ct.POINTER(Hyper)]
+    L.oracle_adam_f32.argtypes = [U64, P, P, P, P, ct.POINTER(Hyper)]
+    L.oracle_owner_step.argtypes = [ct.c_uint32, I, P, U64, P, F, U64, P, P, P, P, P, U64, P,
+                                    I, U64, ct.POINTER(Hyper)]
+    L.oracle_num_threads.restype = I
+    return L
 
 
 def lib():
@@ -227,28 +257,7 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             build()
-        L = ct.CDLL(LIB_PATH)
-        P, U64, F, D, I = ct.c_void_p, ct.c_uint64, ct.c_float, ct.c_double, ct.c_int
-        L.oracle_f32_to_f16.restype = ct.c_uint16
-        L.oracle_f32_to_f16.argtypes = [F]
-        L.oracle_f32_to_bf16.restype = ct.c_uint16
-        L.oracle_f32_to_bf16.argtypes = [F]
-        L.oracle_f16_value.restype = D
-        L.oracle_f16_value.argtypes = [ct.c_uint16]
-        L.oracle_bf16_value.restype = D
-        L.oracle_bf16_value.argtypes = [ct.c_uint16]
-        L.oracle_encode16.argtypes = [P, U64, I, P]
-        L.oracle_reduce.argtypes = [ct.c_uint32, I, P, U64, F, I, P]
-        L.oracle_accumulate.argtypes = [I, P, U64, I, P]
-        L.oracle_grad_check.argtypes = [P, U64, P, P]
-        L.oracle_clip_coef.restype = D
-        L.oracle_clip_coef.argtypes = [D, D, D]
-        L.oracle_adam_f64.argtypes = [U64, P, P, P, P, ct.POINTER(Hyper)]
-        L.oracle_adam_f32.argtypes = [U64, P, P, P, P, ct.POINTER(Hyper)]
-        L.oracle_owner_step.argtypes = [ct.c_uint32, I, P, U64, P, F, U64, P, P, P, P, P, U64, P,
-                                        I, U64, ct.POINTER(Hyper)]
-        L.oracle_num_threads.restype = I
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
 
 

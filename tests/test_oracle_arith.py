@@ -315,7 +315,7 @@ def test_owner_step_is_reduce_then_adam_then_cast_over_real_elements():
     offsets, total, owners = oracle.layout(numels, R, A)
     grads = [(rng.standard_normal(total) * 1e-3).astype(np.float16).view(np.uint16) for _ in range(R)]
     h = oracle.hyper(lr=1e-3, beta1=0.8, beta2=0.999, eps=1e-8, weight_decay=3e-7, step=2)
-    for b, e in owners:
+    for (b, e), pdtype in zip(owners, (BF16, F16, BF16)):
         lb = b & ~7
         size = e - lb
         w = (rng.standard_normal(size) * 0.02).astype(np.float32)
@@ -325,7 +325,7 @@ def test_owner_step_is_reduce_then_adam_then_cast_over_real_elements():
         w1, m1, v1 = w.copy(), m.copy(), v.copy()
         ranges = oracle.real_ranges(numels, offsets, b, e)
         oracle.owner_step(ranges, h, w1, m1, v1, lb, grads=grads, gdtype=F16, divisor=float(R),
-                          p16=p16, pdtype=BF16)
+                          p16=p16, pdtype=pdtype)
         g = oracle.reduce(grads, F16, float(R))
         real = np.zeros(total, dtype=bool)
         for rb, re_ in ranges:
@@ -338,5 +338,5 @@ def test_owner_step_is_reduce_then_adam_then_cast_over_real_elements():
         w2[loc], m2[loc], v2[loc] = ww, mm, vv
         assert np.array_equal(w1, w2) and np.array_equal(m1, m2) and np.array_equal(v1, v2)
         want = np.full(total, 0xABCD, dtype=np.uint16)
-        want[idx] = oracle.encode16(ww, BF16)
+        want[idx] = oracle.encode16(ww, pdtype)
         assert np.array_equal(p16, want)  # padding and other owners untouched
