@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4, 5))
     ap.add_argument("--grid", type=int, default=0, help="persistent grid blocks (0: library default)")
-    ap.add_argument("--chunk", type=int, default=16384, help="max chunk elements")
+    ap.add_argument("--chunk", type=int, default=4096, help="max chunk elements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     return ap.parse_args()
@@ -153,6 +153,7 @@ class Workload:
         if cfg == 5:
             self._setup_microsteps(seed)
         self.t = FIRST_STEP
+        self.calls = 0
         self.skipped = 0
         self.kernel_bytes = self.algorithmic_bytes()
         torch.cuda.synchronize()
@@ -216,8 +217,9 @@ class Workload:
         if self.cfg == 5:
             for k, g in enumerate(self.micro):
                 zs.zero_reduce_owned([g], 0, sh.padded_total, 1.0, self.acc, accumulate=k > 0)
+        self.calls += 1
         if self.cfg == 4:
-            inject = (self.t - FIRST_STEP) % 4 == 3
+            inject = self.calls % 4 == 0  # one step in four carries an inf and a NaN
             if inject:  # +inf in one rank, NaN in another (input preparation, two stores)
                 self.grads[5][12345] = float("inf")
                 self.grads[17][777_777] = float("nan")

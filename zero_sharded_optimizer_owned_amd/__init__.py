@@ -61,6 +61,24 @@ class Ratio(ct.Structure):
 _lib = None
 
 
+def load(path: str):
+    """Open a build of libzero_shard and declare its signatures."""
+    L = ct.CDLL(path)
+    P, U32, U64, I, F, D = ct.c_void_p, ct.c_uint32, ct.c_uint64, ct.c_int, ct.c_float, ct.c_double
+    L.zero_last_error.restype = ct.c_char_p
+    L.zero_last_error.argtypes = []
+    for name in EXPORTED[1:]:
+        getattr(L, name).restype = I
+    L.zero_shard_layout.argtypes = [P, U32, U32, U32, P, P, P, P]
+    L.zero_chunk_table.argtypes = [P, P, U32, U64, U64, U32, P, U64, P]
+    L.zero_state_bytes.argtypes = [U64, U64, U32, U32, U32, P]
+    L.zero_reduce_owned.argtypes = [P, U32, I, U64, U64, U64, F, I, P, U64, P, P, P, ct.c_size_t, P]
+    L.zero_grad_check.argtypes = [P, U64, P, P, P, ct.c_size_t, P]
+    L.zero_clip_coef.argtypes = [D, D, D, ct.POINTER(F)]
+    L.zero_adam_step.argtypes = [ct.POINTER(AdamArgs), P]
+    return L
+
+
 def lib():
     """The loaded library; raises if it has not been built."""
     global _lib
@@ -68,20 +86,7 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
                                "(there is no fallback path)")
-        L = ct.CDLL(LIB_PATH)
-        P, U32, U64, I, F, D = ct.c_void_p, ct.c_uint32, ct.c_uint64, ct.c_int, ct.c_float, ct.c_double
-        L.zero_last_error.restype = ct.c_char_p
-        L.zero_last_error.argtypes = []
-        for name in EXPORTED[1:]:
-            getattr(L, name).restype = I
-        L.zero_shard_layout.argtypes = [P, U32, U32, U32, P, P, P, P]
-        L.zero_chunk_table.argtypes = [P, P, U32, U64, U64, U32, P, U64, P]
-        L.zero_state_bytes.argtypes = [U64, U64, U32, U32, U32, P]
-        L.zero_reduce_owned.argtypes = [P, U32, I, U64, U64, U64, F, I, P, U64, P, P, P, ct.c_size_t, P]
-        L.zero_grad_check.argtypes = [P, U64, P, P, P, ct.c_size_t, P]
-        L.zero_clip_coef.argtypes = [D, D, D, ct.POINTER(F)]
-        L.zero_adam_step.argtypes = [ct.POINTER(AdamArgs), P]
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
 
 
@@ -292,7 +297,7 @@ class OwnerShard:
     """
 
     def __init__(self, numels: Sequence[int], ranks: int, owner: int, align: int = 64,
-                 max_chunk: int = 16384, device=None):
+                 max_chunk: int = 4096, device=None):
         torch = _torch()
         self.numels = [int(x) for x in numels]
         self.offsets, self.padded_total, begins, ends = zero_shard_layout(self.numels, ranks, align)

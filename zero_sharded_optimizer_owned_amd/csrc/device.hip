@@ -154,40 +154,77 @@ __device__ __forceinline__ float divide(float s, const RankSet& rs) {
   return rs.div_pow2 ? s * rs.inv_divisor : s / rs.divisor;
 }
 
+// The same division for whole vectors, with the (uniform) test taken once.
+template <int U>
+__device__ __forceinline__ void divide_vec(float (&s)[U][8], const RankSet& rs) {
+  if (rs.div_pow2) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s[u][k] = s[u][k] * rs.inv_divisor;
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s[u][k] = s[u][k] / rs.divisor;
+  }
+}
+
 // Batch of ranks whose loads are issued together before their adds.
 template <int DT>
 struct RankBatch {
   static constexpr int value = DT == ZERO_F32 ? 4 : 8;  // 32 VGPRs of raw data per vector
 };
 
+template <int DT, int U, int B>
+__device__ __forceinline__ void load_batch(const RankSet& rs, uint32_t r0, const uint64_t (&f)[U],
+                                           typename Elem<DT>::Raw (&x)[B][U]) {
+#pragma unroll
+  for (int j = 0; j < B; ++j)
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[j][u] = Elem<DT>::load_raw(rs.ptr[r0 + j], f[u] - rs.base);
+}
+
+template <int DT, int U, int B>
+__device__ __forceinline__ void add_batch(const typename Elem<DT>::Raw (&x)[B][U], float (&s)[U][8]) {
+#pragma unroll
+  for (int j = 0; j < B; ++j)
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s[u][k] = s[u][k] + Elem<DT>::widen(x[j][u], k);
+}
+
+// s += g_0 + ... + g_{R-1} (in rank order) for a runtime R, then divide.
+// Whole batches are double-buffered: batch b+1 is in flight while batch b is
+// added; the last R mod B ranks follow one at a time.
 template <int DT, int U>
 __device__ __forceinline__ void reduce_vec(const RankSet& rs, const uint64_t (&f)[U],
                                            float (&s)[U][8]) {
   constexpr int B = RankBatch<DT>::value;
   typedef typename Elem<DT>::Raw Raw;
-  for (uint32_t r0 = 0; r0 < rs.R; r0 += B) {
-    Raw x[B][U];
-#pragma unroll
-    for (int j = 0; j < B; ++j) {
-      if (r0 + j < rs.R) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) x[j][u] = Elem<DT>::load_raw(rs.ptr[r0 + j], f[u] - rs.base);
-      }
+  const uint32_t full = rs.R / B * B;
+  uint32_t r0 = 0;
+  if (full > 0) {
+    Raw xa[B][U], xb[B][U];
+    load_batch<DT, U, B>(rs, 0, f, xa);
+    for (; r0 + 2 * B <= full; r0 += 2 * B) {
+      load_batch<DT, U, B>(rs, r0 + B, f, xb);
+      add_batch<DT, U, B>(xa, s);
+      if (r0 + 2 * B < full) load_batch<DT, U, B>(rs, r0 + 2 * B, f, xa);
+      add_batch<DT, U, B>(xb, s);
     }
-#pragma unroll
-    for (int j = 0; j < B; ++j) {
-      if (r0 + j < rs.R) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-          for (int k = 0; k < 8; ++k) s[u][k] = s[u][k] + Elem<DT>::widen(x[j][u], k);
-      }
+    if (r0 < full) {  // an odd number of whole batches: the last one is in xa
+      add_batch<DT, U, B>(xa, s);
+      r0 += B;
     }
   }
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) s[u][k] = divide(s[u][k], rs);
+  for (; r0 < rs.R; ++r0) {
+    Raw x[1][U];
+    load_batch<DT, U, 1>(rs, r0, f, x);
+    add_batch<DT, U, 1>(x, s);
+  }
+  divide_vec<U>(s, rs);
 }
 
 template <int DT>
@@ -371,25 +408,58 @@ struct AdamArgs {
   AdamConst c;
 };
 
-template <int GDT, int PDT, bool REDUCED, int U>
+// Gradient source of the fused step, fixed at compile time:
+//   RC > 0  : exactly RC rank buffers (all loads unrolled, none guarded);
+//   RC == 0 : any number of rank buffers, loaded in double-buffered batches;
+//   RC == kReduced : a stored owner-local fp32 reduced gradient.
+constexpr int kReduced = -1;
+
+// Vectors per lane per iteration: two while the gradient loads of both fit in
+// about 64 VGPRs, else one.
+template <int GDT, int RC>
+struct StepUnroll {
+  static constexpr int loads = RC == kReduced ? 2 : RC * (GDT == ZERO_F32 ? 2 : 1);
+  static constexpr int value = (RC != 0 && loads <= 8) ? 2 : 1;
+};
+
+template <int GDT, int PDT, int RC, int U>
 __device__ __forceinline__ void adam_vec(const AdamArgs& a, const uint64_t (&f)[U]) {
-  float g[U][8];
-  if (REDUCED) {
+  float g[U][8], w[U][8], m[U][8], v[U][8];
 #pragma unroll
-    for (int u = 0; u < U; ++u) load8f(a.reduced_g, f[u] - a.local_base, g[u]);
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) g[u][k] = 0.0f;
+  // Every load of the iteration is issued before the first add: one memory
+  // round trip per iteration.
+  if constexpr (RC > 0) {
+    typename Elem<GDT>::Raw x[RC][U];
+    load_batch<GDT, U, RC>(a.rs, 0, f, x);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      load8f(a.w, f[u] - a.local_base, w[u]);
+      load8f(a.m, f[u] - a.local_base, m[u]);
+      load8f(a.v, f[u] - a.local_base, v[u]);
+    }
+    // Keep the scheduler from sinking the state loads below the adds.
+    __builtin_amdgcn_sched_barrier(0);
+    add_batch<GDT, U, RC>(x, g);
+    divide_vec<U>(g, a.rs);
+  } else if constexpr (RC == kReduced) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      load8f(a.reduced_g, f[u] - a.local_base, g[u]);
+      load8f(a.w, f[u] - a.local_base, w[u]);
+      load8f(a.m, f[u] - a.local_base, m[u]);
+      load8f(a.v, f[u] - a.local_base, v[u]);
+    }
   } else {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) g[u][k] = 0.0f;
+    for (int u = 0; u < U; ++u) {
+      load8f(a.w, f[u] - a.local_base, w[u]);
+      load8f(a.m, f[u] - a.local_base, m[u]);
+      load8f(a.v, f[u] - a.local_base, v[u]);
+    }
     reduce_vec<GDT, U>(a.rs, f, g);
-  }
-  float w[U][8], m[U][8], v[U][8];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    load8f(a.w, f[u] - a.local_base, w[u]);
-    load8f(a.m, f[u] - a.local_base, m[u]);
-    load8f(a.v, f[u] - a.local_base, v[u]);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -402,9 +472,10 @@ __device__ __forceinline__ void adam_vec(const AdamArgs& a, const uint64_t (&f)[
   }
 }
 
-template <int GDT, int PDT, bool REDUCED>
+template <int GDT, int PDT, int RC>
 __device__ __forceinline__ void adam_one(const AdamArgs& a, uint64_t f) {
-  const float g = REDUCED ? a.reduced_g[f - a.local_base] : reduce_one<GDT>(a.rs, f, 0.0f);
+  const float g =
+      RC == kReduced ? a.reduced_g[f - a.local_base] : reduce_one<GDT>(a.rs, f, 0.0f);
   const uint64_t l = f - a.local_base;
   float w = a.w[l], m = a.m[l], v = a.v[l];
   adam_update(g, w, m, v, a.c);
@@ -414,33 +485,44 @@ __device__ __forceinline__ void adam_one(const AdamArgs& a, uint64_t f) {
   if constexpr (PDT != ZERO_NONE) Elem<PDT>::store1(a.p16, f - a.param_base, w);
 }
 
-template <int GDT, int PDT, bool REDUCED>
+// Persistent multi-tensor kernel: wavefront `wave` takes chunks wave,
+// wave + n_waves, ...; the next chunk's descriptor is fetched while the
+// current chunk streams.
+template <int GDT, int PDT, int RC>
 __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs a) {
+  constexpr int U = StepUnroll<GDT, RC>::value;
   const uint32_t lane = threadIdx.x & 63;
   const uint64_t wave =
       __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   const uint64_t n_waves = (uint64_t)gridDim.x * kWavesPerBlock;
+  if (wave >= a.n_chunks) return;
+  zero_chunk ch = a.chunks[wave];
   for (uint64_t c = wave; c < a.n_chunks; c += n_waves) {
-    const zero_chunk ch = a.chunks[c];
+    zero_chunk next = ch;
+    if (c + n_waves < a.n_chunks) next = a.chunks[c + n_waves];
     const uint64_t f0 = max(ch.flat, a.begin);
     const uint64_t f1 = min(ch.flat + ch.len, a.end);
-    if (f0 >= f1) continue;
-    const uint64_t a0 = min(f1, (f0 + 7) & ~7ull);
-    const uint64_t a1 = max(a0, f1 & ~7ull);
-    // Scalar peels: lanes 0-6 take the head before the first vector boundary,
-    // lanes 8-14 the tail after the last one.
-    if (lane < a0 - f0) adam_one<GDT, PDT, REDUCED>(a, f0 + lane);
-    else if (lane >= 8 && lane - 8 < f1 - a1) adam_one<GDT, PDT, REDUCED>(a, a1 + lane - 8);
-    uint64_t vi = a0 / 8 + lane;
-    const uint64_t vend = a1 / 8;
-    for (; vi + 64 < vend; vi += 128) {
-      const uint64_t f[2] = {vi * 8, (vi + 64) * 8};
-      adam_vec<GDT, PDT, REDUCED, 2>(a, f);
+    if (f0 < f1) {
+      const uint64_t a0 = min(f1, (f0 + 7) & ~7ull);
+      const uint64_t a1 = max(a0, f1 & ~7ull);
+      // Scalar peels: lanes 0-6 take the head before the first vector
+      // boundary, lanes 8-14 the tail after the last one.
+      if (lane < a0 - f0) adam_one<GDT, PDT, RC>(a, f0 + lane);
+      else if (lane >= 8 && lane - 8 < f1 - a1) adam_one<GDT, PDT, RC>(a, a1 + lane - 8);
+      uint64_t vi = a0 / 8 + lane;
+      const uint64_t vend = a1 / 8;
+      if constexpr (U == 2) {
+        for (; vi + 64 < vend; vi += 128) {
+          const uint64_t f[2] = {vi * 8, (vi + 64) * 8};
+          adam_vec<GDT, PDT, RC, 2>(a, f);
+        }
+      }
+      for (; vi < vend; vi += 64) {
+        const uint64_t f[1] = {vi * 8};
+        adam_vec<GDT, PDT, RC, 1>(a, f);
+      }
     }
-    if (vi < vend) {
-      const uint64_t f[1] = {vi * 8};
-      adam_vec<GDT, PDT, REDUCED, 1>(a, f);
-    }
+    ch = next;
   }
 }
 
@@ -547,11 +629,48 @@ void launch_reduce(const ReduceArgs& a, bool accum, bool check, uint32_t grid, h
   }
 }
 
-template <int GDT, bool REDUCED>
-void launch_adam_p(const AdamArgs& a, int pdt, uint32_t grid, hipStream_t s) {
-  if (pdt == ZERO_F16) hipLaunchKernelGGL((adam_kernel<GDT, ZERO_F16, REDUCED>), grid, kBlock, 0, s, a);
-  else if (pdt == ZERO_BF16) hipLaunchKernelGGL((adam_kernel<GDT, ZERO_BF16, REDUCED>), grid, kBlock, 0, s, a);
-  else hipLaunchKernelGGL((adam_kernel<GDT, ZERO_NONE, REDUCED>), grid, kBlock, 0, s, a);
+// Blocks of `kernel` that fit on one CU at once.
+template <typename K>
+uint32_t blocks_per_cu(K kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kBlock, 0) != hipSuccess || n < 1) n = 1;
+  return (uint32_t)n;
+}
+
+// A persistent grid: every block resident at once, but no more blocks than
+// there are chunks for their wavefronts.
+uint32_t persistent_grid(uint32_t per_cu, uint64_t n_chunks, int cus, uint32_t requested) {
+  if (requested) return requested;
+  const uint64_t resident = (uint64_t)per_cu * (uint64_t)cus;
+  const uint64_t by_chunks = (n_chunks + kWavesPerBlock - 1) / kWavesPerBlock;
+  return (uint32_t)(by_chunks < resident ? by_chunks : resident);
+}
+
+template <int GDT, int PDT, int RC>
+void launch_adam_k(const AdamArgs& a, int cus, uint32_t grid, hipStream_t s) {
+  const auto k = adam_kernel<GDT, PDT, RC>;
+  static const uint32_t per_cu = blocks_per_cu(k);  // one query per instantiation
+  hipLaunchKernelGGL(k, persistent_grid(per_cu, a.n_chunks, cus, grid), kBlock, 0, s, a);
+}
+
+template <int GDT, int RC>
+void launch_adam_p(const AdamArgs& a, int pdt, int cus, uint32_t grid, hipStream_t s) {
+  if (pdt == ZERO_F16) launch_adam_k<GDT, ZERO_F16, RC>(a, cus, grid, s);
+  else if (pdt == ZERO_BF16) launch_adam_k<GDT, ZERO_BF16, RC>(a, cus, grid, s);
+  else launch_adam_k<GDT, ZERO_NONE, RC>(a, cus, grid, s);
+}
+
+// Rank counts with a fully unrolled kernel; any other count takes the batched one.
+template <int GDT>
+void launch_adam_r(const AdamArgs& a, int pdt, int cus, uint32_t grid, hipStream_t s) {
+  switch (a.rs.R) {
+    case 1: launch_adam_p<GDT, 1>(a, pdt, cus, grid, s); break;
+    case 2: launch_adam_p<GDT, 2>(a, pdt, cus, grid, s); break;
+    case 4: launch_adam_p<GDT, 4>(a, pdt, cus, grid, s); break;
+    case 8: launch_adam_p<GDT, 8>(a, pdt, cus, grid, s); break;
+    case 16: launch_adam_p<GDT, 16>(a, pdt, cus, grid, s); break;
+    default: launch_adam_p<GDT, 0>(a, pdt, cus, grid, s); break;
+  }
 }
 
 }  // namespace
@@ -692,19 +811,14 @@ extern "C" int zero_adam_step(const zero_adam_args* p, hipStream_t stream) {
   a.p16 = pdt != ZERO_NONE ? p->param16 : nullptr;
   a.param_base = p->param_base;
 
-  uint32_t grid = p->grid_blocks;
-  if (grid == 0) {
-    const uint64_t by_chunks = (p->n_chunks + kWavesPerBlock - 1) / kWavesPerBlock;
-    const uint64_t full = (uint64_t)cus * 8;
-    grid = (uint32_t)(by_chunks < full ? by_chunks : full);
-  }
+  const uint32_t grid = p->grid_blocks;
   if (reduced) {
-    launch_adam_p<ZERO_F32, true>(a, pdt, grid, stream);
+    launch_adam_p<ZERO_F32, kReduced>(a, pdt, cus, grid, stream);
   } else {
     switch (p->grad_dtype) {
-      case ZERO_F16: launch_adam_p<ZERO_F16, false>(a, pdt, grid, stream); break;
-      case ZERO_BF16: launch_adam_p<ZERO_BF16, false>(a, pdt, grid, stream); break;
-      default: launch_adam_p<ZERO_F32, false>(a, pdt, grid, stream); break;
+      case ZERO_F16: launch_adam_r<ZERO_F16>(a, pdt, cus, grid, stream); break;
+      case ZERO_BF16: launch_adam_r<ZERO_BF16>(a, pdt, cus, grid, stream); break;
+      default: launch_adam_r<ZERO_F32>(a, pdt, cus, grid, stream); break;
     }
   }
   return launch_status(who);
