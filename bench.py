@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--chunk", type=int, default=4096, help="max chunk elements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB fp32 device copy (counter calibration)")
     return ap.parse_args()
 
 
@@ -221,6 +223,7 @@ class Workload:
         if self.cfg == 4:
             inject = self.calls % 4 == 0  # one step in four carries an inf and a NaN
             if inject:  # +inf in one rank, NaN in another (input preparation, two stores)
+                saved = (self.grads[5][12345].clone(), self.grads[17][777_777].clone())
                 self.grads[5][12345] = float("inf")
                 self.grads[17][777_777] = float("nan")
             zs.zero_reduce_owned(self.grads, sh.begin, sh.end - sh.begin, self.divisor, self.g32,
@@ -228,8 +231,8 @@ class Workload:
                                  check=(self.ov, self.ss, self.ws))
             flag, sumsq = int(self.ov.item()), float(self.ss.item())  # 12 bytes to the host
             if inject:
-                self.grads[5][12345] = 0.0
-                self.grads[17][777_777] = 0.0
+                self.grads[5][12345] = saved[0]
+                self.grads[17][777_777] = saved[1]
             if flag:
                 self.skipped += 1
                 return True
@@ -337,6 +340,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     zs.lib()
+    if args.calibrate_copy:
+        # a plain copy of known size: 2^28 fp32 read + 2^28 fp32 written per launch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = Workload(args.config, args.chunk, args.grid)
     for _ in range(args.warmup):
         w.step()
