@@ -34,6 +34,11 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / 64;
 constexpr int kMaxPartials = 4096;  // per-block partials the check workspace holds
+// Flat-range kernels hand out work in tiles: one wavefront streams a contiguous
+// span of every stream (up to 512 vectors = 4096 elements) before taking the
+// next tile with a grid stride.  Short ranges use shorter tiles (down to one
+// vector per lane) so that every CU still gets work.
+constexpr uint64_t kMaxTileVectors = 512;
 static_assert(kMaxPartials * (sizeof(double) + sizeof(int32_t)) <= ZERO_CHECK_WS_BYTES,
               "check workspace too small");
 
@@ -284,6 +289,7 @@ struct CheckOut {
 struct ReduceArgs {
   RankSet rs;
   uint64_t begin, end;
+  uint64_t tile;  // vectors per wavefront tile
   float* out;
   uint64_t out_base;
   CheckOut chk;
@@ -308,21 +314,27 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs a) {
       if (CHECK) check_accum(g, sq, bad);
     }
   }
-  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
-  for (uint64_t v = a0 / 8 + (uint64_t)blockIdx.x * kBlock + threadIdx.x; v < a1 / 8; v += stride) {
-    const uint64_t f[1] = {v * 8};
-    float s[1][8];
-    if (ACCUM) {
-      load8f(a.out, f[0] - a.out_base, s[0]);
-    } else {
+  const uint64_t v0 = a0 / 8, n_vec = a1 / 8 - v0;
+  const uint64_t lane = threadIdx.x & 63;
+  const uint64_t wave = (uint64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const uint64_t n_waves = (uint64_t)gridDim.x * kWavesPerBlock;
+  for (uint64_t t0 = wave * a.tile; t0 < n_vec; t0 += n_waves * a.tile) {
+    const uint64_t t1 = min(n_vec, t0 + a.tile);
+    for (uint64_t v = t0 + lane; v < t1; v += 64) {
+      const uint64_t f[1] = {(v0 + v) * 8};
+      float s[1][8];
+      if (ACCUM) {
+        load8f(a.out, f[0] - a.out_base, s[0]);
+      } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) s[0][k] = 0.0f;
-    }
-    reduce_vec<DT, 1>(a.rs, f, s);
-    Elem<ZERO_F32>::store8(a.out, f[0] - a.out_base, s[0]);
-    if (CHECK) {
+        for (int k = 0; k < 8; ++k) s[0][k] = 0.0f;
+      }
+      reduce_vec<DT, 1>(a.rs, f, s);
+      Elem<ZERO_F32>::store8(a.out, f[0] - a.out_base, s[0]);
+      if (CHECK) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) check_accum(s[0][k], sq, bad);
+        for (int k = 0; k < 8; ++k) check_accum(s[0][k], sq, bad);
+      }
     }
   }
   if (CHECK) {
@@ -337,17 +349,24 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs a) {
 // ---------------------------------------------------------------------------
 // K2: check of a stored fp32 gradient (first stage), and the final stage.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kBlock) check_kernel(const float* g, uint64_t n, CheckOut chk) {
+__global__ void __launch_bounds__(kBlock) check_kernel(const float* g, uint64_t n, uint64_t tile,
+                                                       CheckOut chk) {
   const uint64_t a1 = n & ~7ull;
   double sq = 0.0;
   int bad = 0;
   if (blockIdx.x == 0 && threadIdx.x < n - a1) check_accum(g[a1 + threadIdx.x], sq, bad);
-  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
-  for (uint64_t v = (uint64_t)blockIdx.x * kBlock + threadIdx.x; v < a1 / 8; v += stride) {
-    float x[8];
-    load8f(g, v * 8, x);
+  const uint64_t n_vec = a1 / 8;
+  const uint64_t lane = threadIdx.x & 63;
+  const uint64_t wave = (uint64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const uint64_t n_waves = (uint64_t)gridDim.x * kWavesPerBlock;
+  for (uint64_t t0 = wave * tile; t0 < n_vec; t0 += n_waves * tile) {
+    const uint64_t t1 = min(n_vec, t0 + tile);
+    for (uint64_t v = t0 + lane; v < t1; v += 64) {
+      float x[8];
+      load8f(g, v * 8, x);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) check_accum(x[k], sq, bad);
+      for (int k = 0; k < 8; ++k) check_accum(x[k], sq, bad);
+    }
   }
   block_reduce(sq, bad);
   if (threadIdx.x == 0) {
@@ -604,12 +623,26 @@ CheckOut check_layout(void* ws) {
   return c;
 }
 
-uint32_t stream_grid(uint64_t n_vectors, int cus, uint32_t cap) {
-  uint64_t want = (n_vectors + kBlock - 1) / kBlock;
-  const uint64_t full = (uint64_t)cus * 8;  // eight 256-thread blocks per CU
-  if (want > full) want = full;
-  if (want > cap) want = cap;
-  return want == 0 ? 1u : (uint32_t)want;
+// Launch shape of a flat-range kernel: at most eight 256-thread blocks per CU
+// and `cap` blocks; the tile is the longest (<= 512 vectors, a multiple of 64)
+// that still gives every wavefront of that grid a tile.
+struct FlatPlan {
+  uint32_t grid;
+  uint64_t tile;
+};
+
+FlatPlan flat_plan(uint64_t n_vectors, int cus, uint32_t cap) {
+  uint64_t blocks = (uint64_t)cus * 8;
+  if (blocks > cap) blocks = cap;
+  const uint64_t waves = blocks * kWavesPerBlock;
+  uint64_t tile = (n_vectors + waves - 1) / waves;
+  tile = (tile + 63) / 64 * 64;
+  if (tile < 64) tile = 64;
+  if (tile > kMaxTileVectors) tile = kMaxTileVectors;
+  const uint64_t tiles = (n_vectors + tile - 1) / tile;
+  uint64_t want = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (want > blocks) want = blocks;
+  return FlatPlan{want == 0 ? 1u : (uint32_t)want, tile};
 }
 
 int launch_status(const char* who) {
@@ -708,7 +741,9 @@ extern "C" int zero_reduce_owned(const void* const* rank_grads, uint32_t R, int 
   a.out = out;
   a.out_base = out_base;
   if (check) a.chk = check_layout(workspace);
-  const uint32_t grid = stream_grid((n + 7) / 8, cus, kMaxPartials);
+  const FlatPlan plan = flat_plan((n + 7) / 8, cus, kMaxPartials);
+  const uint32_t grid = plan.grid;
+  a.tile = plan.tile;
   switch (grad_dtype) {
     case ZERO_F16: launch_reduce<ZERO_F16>(a, accumulate != 0, check, grid, stream); break;
     case ZERO_BF16: launch_reduce<ZERO_BF16>(a, accumulate != 0, check, grid, stream); break;
@@ -733,9 +768,10 @@ extern "C" int zero_grad_check(const float* g, uint64_t n, int32_t* d_overflow, 
   if (n > 0 && !aligned16(g)) return fail(ZERO_EINVAL, "%s: g is not 16-byte aligned", who);
   int cus = 0;
   if ((rc = cu_count(&cus))) return rc;
-  const uint32_t grid = stream_grid(n / 8, cus, kMaxPartials);
+  const FlatPlan plan = flat_plan(n / 8, cus, kMaxPartials);
+  const uint32_t grid = plan.grid;
   const CheckOut chk = check_layout(workspace);
-  hipLaunchKernelGGL(check_kernel, grid, kBlock, 0, stream, g, n, chk);
+  hipLaunchKernelGGL(check_kernel, grid, kBlock, 0, stream, g, n, plan.tile, chk);
   if ((rc = launch_status(who))) return rc;
   hipLaunchKernelGGL(check_final_kernel, 1, kBlock, 0, stream, chk, grid, d_overflow, d_sumsq);
   return launch_status(who);
