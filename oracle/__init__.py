@@ -240,6 +240,7 @@ def load(path: str):
     L.oracle_bf16_value.argtypes = [ct.c_uint16]
     L.oracle_encode16.argtypes = [P, U64, I, P]
     L.oracle_reduce.argtypes = [ct.c_uint32, I, P, U64, F, I, P]
+    L.oracle_reduce_add.argtypes = [ct.c_uint32, I, P, U64, F, P]
     L.oracle_accumulate.argtypes = [I, P, U64, I, P]
     L.oracle_grad_check.argtypes = [P, U64, P, P]
     L.oracle_clip_coef.restype = D
@@ -308,6 +309,21 @@ def reduce(grads: Sequence[np.ndarray], dtype: int, divisor: float, out: np.ndar
         out = np.empty(n, dtype=np.float32)
     lib().oracle_reduce(len(grads), dtype, _ptr_array(grads), n, divisor, int(accumulate),
                         _ptr(out))
+    return out
+
+
+def reduce_add(grads: Sequence[np.ndarray], dtype: int, divisor: float, out: np.ndarray) -> np.ndarray:
+    """Per-backward reduce-and-accumulate: ``out += (g_0 + ... + g_{R-1}) / divisor``,
+    the reduced value rounded to fp32 before the fp32 add."""
+    n = grads[0].size
+    for g in grads:
+        _storage(g, dtype)
+        if g.size != n:
+            raise ValueError("rank buffers differ in length")
+    _storage(out, F32)
+    if out.size != n:
+        raise ValueError("accumulator and rank buffers differ in length")
+    lib().oracle_reduce_add(len(grads), dtype, _ptr_array(grads), n, divisor, _ptr(out))
     return out
 
 

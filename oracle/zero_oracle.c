@@ -131,6 +131,21 @@ void oracle_reduce(uint32_t R, int dtype, const void *const *grads, uint64_t n, 
     out[i] = reduce_one(R, dtype, grads, (uint64_t)i, accumulate ? out[i] : 0.0f, divisor);
 }
 
+/* Per-backward reduce-and-accumulate ([Deep dive] "Communication volume isn't
+ * elapsed time": by default ZeRO-2 and ZeRO-3 reduce and partition gradients
+ * on every backward call and keep only the owned slice until the optimizer
+ * step).  Each microstep's owned gradient is reduced first, rounded to fp32,
+ * then added to the accumulator in fp32:
+ *   out[i] = out[i] + (g_0[i] + ... + g_{R-1}[i]) / divisor. */
+void oracle_reduce_add(uint32_t R, int dtype, const void *const *grads, uint64_t n, float divisor,
+                       float *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < (int64_t)n; ++i) {
+    const float reduced = reduce_one(R, dtype, grads, (uint64_t)i, 0.0f, divisor);
+    out[i] = out[i] + reduced;
+  }
+}
+
 /* Gradient accumulation in an fp32 array ([Deep dive] "Count state before
  * choosing a stage" and "Let the engine own the microstep": a four-byte
  * accumulation buffer replaces the two-byte gradient).  first != 0 starts the

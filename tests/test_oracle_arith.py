@@ -340,3 +340,42 @@ def test_owner_step_is_reduce_then_adam_then_cast_over_real_elements():
         want = np.full(total, 0xABCD, dtype=np.uint16)
         want[idx] = oracle.encode16(ww, pdtype)
         assert np.array_equal(p16, want)  # padding and other owners untouched
+
+
+# ---------------------------------------------------------------- per-backward reduce + accumulate
+def test_reduce_add_dyadic_microsteps_are_exact():
+    rng = np.random.default_rng(16)
+    R, K, n = 8, 6, 3000
+    ks = rng.integers(-1024, 1025, size=(K, R, n))
+    acc = np.zeros(n, dtype=np.float32)
+    for k in range(K):
+        grads = [(ks[k, r] * 2.0 ** -10).astype(np.float16).view(np.uint16) for r in range(R)]
+        oracle.reduce_add(grads, F16, float(R), acc)
+    for i in range(0, n, 29):
+        exact = Fraction(int(ks[:, :, i].sum()), 1024 * R)
+        assert acc[i] == _exact_round_f32(exact)
+
+
+def test_reduce_add_rounds_the_mean_before_adding():
+    # Closed forms: the reduced value is rounded to fp32 first, then added.
+    big = np.float32(1e8)
+    acc = np.array([big], dtype=np.float32)
+    g = [np.array([4.0], dtype=np.float32), np.array([4.0], dtype=np.float32)]
+    oracle.reduce_add(g, F32, 1.0, acc)
+    assert acc[0] == big + np.float32(8.0)            # 1e8 + (4 + 4)
+    acc2 = oracle.reduce(g, F32, 1.0, out=np.array([big], dtype=np.float32), accumulate=True)
+    assert acc2[0] == big                               # (1e8 + 4) + 4, ties to even twice
+    # division happens on the fresh sum only: acc + (3 + 5) / 4 = 10 + 2
+    acc = np.array([10.0], dtype=np.float32)
+    oracle.reduce_add([np.array([3.0], dtype=np.float32), np.array([5.0], dtype=np.float32)], F32, 4.0, acc)
+    assert acc[0] == 12.0
+
+
+def test_reduce_add_is_reduce_then_fp32_add():
+    rng = np.random.default_rng(17)
+    grads = [torch.from_numpy(rng.standard_normal(5000).astype(np.float32) * 1e-3).to(torch.bfloat16)
+             .view(torch.int16).numpy().view(np.uint16).copy() for _ in range(5)]
+    acc0 = (rng.standard_normal(5000) * 1e-2).astype(np.float32)
+    got = oracle.reduce_add(grads, BF16, 5.0, acc0.copy())
+    want = (acc0 + oracle.reduce(grads, BF16, 5.0)).astype(np.float32)
+    assert np.array_equal(got, want)

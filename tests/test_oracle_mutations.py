@@ -33,6 +33,7 @@ C_PROBES = [
     A.test_clip_coefficient_scales_the_gradient, PG.test_resume_lab_printed_values,
     A.test_owner_step_is_reduce_then_adam_then_cast_over_real_elements,
     A.test_decoders_are_exact, A.test_f16_encoder_matches_numpy, A.test_bf16_encoder_matches_torch,
+    A.test_reduce_add_rounds_the_mean_before_adding, A.test_reduce_add_dyadic_microsteps_are_exact,
 ]
 
 C_MUTANTS = {
@@ -58,6 +59,9 @@ C_MUTANTS = {
         "g = reduce_one(R, gdtype, grads, (uint64_t)f - local_base, 0.0f, divisor);"),
     "write-back always bf16": ("pdtype == OR_F16 ? oracle_f32_to_f16(wf) : oracle_f32_to_bf16(wf)",
                                "oracle_f32_to_bf16(wf)"),
+    "per-backward add before the division": (
+        "const float reduced = reduce_one(R, dtype, grads, (uint64_t)i, 0.0f, divisor);\n    out[i] = out[i] + reduced;",
+        "out[i] = reduce_one(R, dtype, grads, (uint64_t)i, out[i], divisor);"),
 }
 
 
