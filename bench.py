@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4, 5))
+    ap.add_argument("--schedule", default="accumulate", choices=("accumulate", "per-backward"),
+                    help="config 5 only: accumulate microsteps locally then reduce (default), or reduce "
+                         "every microstep and add the owned mean to an fp32 accumulator")
     ap.add_argument("--grid", type=int, default=0, help="persistent grid blocks (0: library default)")
     ap.add_argument("--chunk", type=int, default=4096, help="max chunk elements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -97,13 +100,16 @@ def fill(t, seed, stream, rank, index0, dist, scale, step=0):
 class Workload:
     """Device buffers and the step function of one configuration."""
 
-    def __init__(self, cfg: int, chunk: int, grid: int):
+    def __init__(self, cfg: int, chunk: int, grid: int, schedule: str = "accumulate"):
         import torch
 
         import synth
         import zero_sharded_optimizer_owned_amd as zs
 
         self.cfg, self.grid = cfg, grid
+        self.schedule = schedule
+        if schedule != "accumulate" and cfg != 5:
+            raise ValueError("--schedule applies to config 5 only")
         dev = torch.device("cuda")
         self.dev = dev
         owner = 1
@@ -152,7 +158,10 @@ class Workload:
             self.p16 = torch.zeros(sh.padded_total, dtype=pdt, device=dev)
             self.param_base = 0
             self.divisor = float(R)
-        if cfg == 5:
+        if cfg == 5 and schedule == "per-backward":
+            self._setup_per_backward(seed)
+            self.name += " (per-backward reduce + fp32 owned accumulator)"
+        elif cfg == 5:
             self._setup_microsteps(seed)
         self.t = FIRST_STEP
         self.calls = 0
@@ -192,11 +201,34 @@ class Workload:
         # the owner's own slice is a view of its accumulation buffer
         self.grads[sh.owner] = self.acc[lb:end]
 
+    def _setup_per_backward(self, seed):
+        """Owner slices of every rank's eight microstep gradients (what a reduce-scatter
+        per backward call delivers) and the owner's fp32 accumulator."""
+        import torch
+
+        import synth
+
+        sh = self.sh
+        lb, end = sh.local_base, sh.end
+        self.micro_slices = []
+        for k in range(8):
+            row = []
+            for r in range(self.R):
+                t = torch.empty(end - lb, dtype=torch.bfloat16, device=self.dev)
+                fill(t, seed, synth.STREAM_MICRO, r, lb, synth.DIST_NORMAL, 1e-3, step=k)
+                row.append(t)
+            self.micro_slices.append(row)
+        self.acc_owned = torch.empty(end - lb, dtype=torch.float32, device=self.dev)
+        self.grads = [None]
+
     def algorithmic_bytes(self) -> int:
         """Bytes the dominant kernel must move per launch."""
         n = self.sh.n_real
         if self.cfg == 4:
             return n * 30  # adam from the stored gradient: g 4 + w,m,v 12 + 12 + p16 2
+        if self.schedule == "per-backward":
+            # one microstep's reduce of 16 bf16 slices into the accumulator: 16*2 + 4 + 4
+            return (self.sh.end - self.sh.begin) * (self.R * 2 + 8)
         gw = self.grads[0].element_size() if self.grads[0] is not None else 4
         return n * (self.R * gw + 24 + self.p16.element_size())
 
@@ -204,6 +236,9 @@ class Workload:
         n = self.sh.n_real
         if self.cfg == 4:
             return n * (self.R * 2 + 4) + (0 if overflow else n * 30)
+        if self.schedule == "per-backward":
+            span = self.sh.end - self.sh.begin
+            return span * (self.R * 2 + 4) + 7 * span * (self.R * 2 + 8) + n * 30
         if self.cfg == 5:
             P = self.sh.padded_total
             return P * (6 + 7 * 10) + self.kernel_bytes
@@ -216,6 +251,19 @@ class Workload:
         import zero_sharded_optimizer_owned_amd as zs
 
         sh = self.sh
+        if self.schedule == "per-backward":
+            for k, row in enumerate(self.micro_slices):
+                if timing is not None and k == 7:
+                    timing[0].record()
+                zs.zero_reduce_owned(row, sh.begin, sh.end - sh.begin, float(self.R), self.acc_owned,
+                                     grad_base=sh.local_base, out_base=sh.local_base,
+                                     accumulate=0 if k == 0 else 2)
+                if timing is not None and k == 7:
+                    timing[1].record()
+            sh.adam_step(step=self.t, hyper=HP, reduced_g=self.acc_owned, param16=self.p16,
+                         param_base=self.param_base, grid_blocks=self.grid)
+            self.t += 1
+            return False
         if self.cfg == 5:
             for k, g in enumerate(self.micro):
                 zs.zero_reduce_owned([g], 0, sh.padded_total, 1.0, self.acc, accumulate=k > 0)
@@ -281,7 +329,18 @@ def cpu_baseline(w: Workload, seconds: float):
     idx = synth.arange(lb, hi)
     gcode = {2: synth.F16, 3: synth.BF16, 4: synth.F16, 5: synth.F32}[cfg]
     scale = w.grad_scale if cfg != 5 else 1e-3
-    if cfg == 5:
+    if w.schedule == "per-backward":
+        # the owner's accumulator: every microstep reduces the ranks' values (untimed)
+        acc = np.zeros(hi - lo, dtype=np.float32)
+        for k in range(8):
+            row = [synth.values(synth.stream_key(seed, synth.STREAM_MICRO, r, k), synth.arange(lo, hi),
+                                synth.DIST_NORMAL, 1e-3, synth.BF16) for r in range(w.R)]
+            if k == 0:
+                acc[:] = oracle.reduce(row, synth.BF16, float(w.R))
+            else:
+                oracle.reduce_add(row, synth.BF16, float(w.R), acc)
+        grads = None
+    elif cfg == 5:
         grads = []
         for r in range(w.R):
             acc = np.zeros(hi - lb, dtype=np.float32)
@@ -304,7 +363,12 @@ def cpu_baseline(w: Workload, seconds: float):
     while True:
         wc, mc, vc = w0.copy(), m0.copy(), v0.copy()
         t_start = time.perf_counter()
-        if cfg == 4:
+        if w.schedule == "per-backward":
+            gfull = np.zeros(hi - lb, dtype=np.float32)
+            gfull[lo - lb:] = acc
+            oracle.owner_step(ranges, oracle.hyper(step=FIRST_STEP, **HP), wc, mc, vc, lb, reduced_g=gfull,
+                              p16=p16, pdtype=pcode, param_base=lb)
+        elif cfg == 4:
             g = oracle.reduce([x[lo - lb:hi - lb] for x in grads], gcode, w.divisor)
             flag, sumsq = oracle.grad_check(g)
             gfull = np.zeros(hi - lb, dtype=np.float32)
@@ -320,10 +384,18 @@ def cpu_baseline(w: Workload, seconds: float):
         reps += 1
         if el >= seconds or reps >= 1000:
             break
+    if w.schedule == "per-backward":
+        what = "AdamW + cast from the owned accumulator; the eight per-microstep reduces untimed"
+    elif cfg == 4:
+        what = "reduce + check + clip + AdamW + cast"
+    elif cfg == 5:
+        what = "reduce + AdamW + cast; the microstep accumulation untimed"
+    else:
+        what = "reduce + AdamW + cast"
     return {"value": done / el, "unit": "params/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"first {n_real} real elements of the owner's shard, {reps} oracle step(s) "
-                      f"({'reduce+check+clip+AdamW' if cfg == 4 else 'reduce+AdamW+cast'}; "
-                      f"{'microstep accumulation untimed; ' if cfg == 5 else ''}inputs pre-generated)"}
+                      f"({what}; inputs pre-generated)"}
+
 
 
 def main():
@@ -348,7 +420,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    w = Workload(args.config, args.chunk, args.grid)
+    w = Workload(args.config, args.chunk, args.grid, args.schedule)
     for _ in range(args.warmup):
         w.step()
     torch.cuda.synchronize()
@@ -380,6 +452,8 @@ def main():
     gbps_step = step_bytes / (total_ms / 1e3) / 1e9
     achieved = w.kernel_bytes / (kernel_ms / 1e3) / 1e9
     kname = "adam_step_" + {2: "f16_f16", 3: "bf16_bf16", 4: "reduced_f16", 5: "f32_bf16"}[args.config]
+    if w.schedule == "per-backward":
+        kname = "reduce_add_mean_bf16_r16"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic_record(f"{kname}_config{args.config}"),
                 "kernel": kname, "kernel_ms": round(kernel_ms, 4),
@@ -389,7 +463,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "config": args.config, "owned_params": n,
+        "config": {"workload": w.name, "config": args.config, "schedule": w.schedule, "owned_params": n,
                    "ranks": w.R, "padded_total": w.sh.padded_total, "chunks": int(w.sh.chunks.size),
                    "parallelism": "1 GPU (owner shard; no collectives)"},
         "gbps": round(gbps_step, 1), "frac_of_peak": round(gbps_step / PEAK_GBPS, 4),

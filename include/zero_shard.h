@@ -151,10 +151,16 @@ int zero_state_bytes(uint64_t params, uint64_t ranks, uint32_t param_bytes, uint
  *
  * [Deep dive] "Reduce first, then update the owned slice" (the reference
  * reduce-scatter: reduce across ranks, keep the owned indices; equally
- * weighted mean).  For every flat index f in [begin, begin + n):
- *   s = (accumulate ? out[f - out_base] : +0.0f);
+ * weighted mean).  For every flat index f in [begin, begin + n), with
+ * o = out[f - out_base]:
+ *   s = (accumulate == 1 ? o : +0.0f);
  *   for r = 0 .. R-1:  s = s + (float) rank_grads[r][f - grad_base];   (fp32)
- *   out[f - out_base] = s / divisor;                                    (IEEE fp32)
+ *   s = s / divisor;                                                    (IEEE fp32)
+ *   out[f - out_base] = (accumulate == 2 ? o + s : s);                  (fp32)
+ * accumulate: 0 overwrite; 1 start the sum from the output; 2 add the
+ * reduced mean to the output -- the per-backward schedule of [Deep dive]
+ * "Communication volume isn't elapsed time" (ZeRO-2/3 reduce and keep the
+ * owned slice on every backward call; Adam runs at the boundary).
  * The order is fixed, so results are identical run to run and bit-exact
  * against a sequential fp32 loop.  A loss scale is folded into `divisor`
  * (e.g. R * 65536).  R = 1, divisor = 1, accumulate = 1 is fp32 gradient
@@ -169,8 +175,8 @@ int zero_state_bytes(uint64_t params, uint64_t ranks, uint32_t param_bytes, uint
  *             device, ZERO_CHECK_WS_BYTES bytes, 256-byte aligned).
  * n == 0 launches nothing (the check outputs are then left untouched).
  * Errors: EINVAL (R out of [1, ZERO_MAX_RANKS], bad dtype, misaligned pointer
- *         or base, begin below a base, divisor not finite and > 0, workspace
- *         missing or too small); EHIP.
+ *         or base, begin below a base, divisor not finite and > 0, accumulate
+ *         not 0, 1 or 2, workspace missing or too small); EHIP.
  * -------------------------------------------------------------------------- */
 int zero_reduce_owned(const void *const *rank_grads, uint32_t R, int grad_dtype, uint64_t grad_base,
                       uint64_t begin, uint64_t n, float divisor, int accumulate, float *out,

@@ -353,3 +353,55 @@ def test_first_step_closed_form_on_gpu():
     assert_state_close(from_dev(w), np.full(8, 1.0 - 0.01 * 2.0 / (2.0 + 1e-8)), "w")
     assert_state_close(from_dev(m), np.full(8, 0.2), "m")
     assert_state_close(from_dev(v), np.full(8, 0.004), "v")
+
+
+# ---------------------------------------------------------------- per-backward reduce + accumulate
+@pytest.mark.parametrize("code", [F16, BF16, F32])
+@pytest.mark.parametrize("R", [1, 6, 16])
+def test_reduce_add_mean_bitexact(code, R):
+    total, begin, n = 40_011, 3, 40_000
+    grads = _rank_inputs(code, R, total, seed=31 + R)
+    start = gen(3, synth.STREAM_EXP_AVG, begin + n, synth.DIST_NORMAL, 1e-2, F32)
+    out = to_dev(start.copy(), F32)
+    zs.zero_reduce_owned([to_dev(g, code) for g in grads], begin, n, float(R), out, accumulate=2)
+    want = start.copy()
+    oracle.reduce_add([g[begin:begin + n] for g in grads], code, float(R), want[begin:])
+    assert_bits_equal(from_dev(out), want, f"add-mean R={R}")
+
+
+def test_per_backward_schedule_matches_oracle():
+    """Four microsteps: each reduces the ranks' owned slices and adds the mean to the
+    owner's fp32 accumulator; AdamW runs once from it at the boundary."""
+    numels, R, A, K = [3000, 77, 20_001, 5], 4, 64, 4
+    off, total, b, e = zs.zero_shard_layout(numels, R, A)
+    owner = 2
+    begin, end = int(b[owner]), int(e[owner])
+    lb = begin & ~7
+    micro = [[gen(40 + k, synth.STREAM_MICRO, total, synth.DIST_NORMAL, 1e-3, BF16, rank=r) for r in range(R)]
+             for k in range(K)]
+    acc_dev = torch.zeros(end - lb, dtype=torch.float32, device=DEV)
+    for k in range(K):
+        slices = [to_dev(m[lb:end], BF16) for m in micro[k]]
+        zs.zero_reduce_owned(slices, begin, end - begin, float(R), acc_dev, grad_base=lb, out_base=lb,
+                             accumulate=0 if k == 0 else 2)
+    acc = np.zeros(end - lb, dtype=np.float32)
+    for k in range(K):
+        if k == 0:
+            acc[begin - lb:] = oracle.reduce([m[begin:end] for m in micro[k]], BF16, float(R))
+        else:
+            oracle.reduce_add([m[begin:end] for m in micro[k]], BF16, float(R), acc[begin - lb:])
+    assert_bits_equal(from_dev(acc_dev)[begin - lb:], acc[begin - lb:], "per-backward accumulator")
+    _, _, _, _, _, _, w, m, v = _owner_inputs(numels, R, A, owner, BF16, 5)
+    chunks = zs.zero_chunk_table(numels, off, begin, end, 512)
+    dw, dm, dv = to_dev(w, F32), to_dev(m, F32), to_dev(v, F32)
+    dp = torch.zeros(total, dtype=torch.bfloat16, device=DEV)
+    zs.zero_adam_step(chunks_dev=zs.chunks_to_device(chunks), n_chunks=chunks.size, begin=begin, end=end,
+                      master=dw, exp_avg=dm, exp_avg_sq=dv, local_base=lb, step=7, reduced_g=acc_dev,
+                      param16=dp, **HP)
+    p_or = np.zeros(total, dtype=np.uint16)
+    oracle.owner_step(oracle.real_ranges(numels, list(off), begin, end), oracle.hyper(step=7, **HP),
+                      w, m, v, lb, reduced_g=acc, p16=p_or, pdtype=BF16)
+    assert_state_close(from_dev(dw), w, "w")
+    assert_state_close(from_dev(dm), m, "m")
+    assert_state_close(from_dev(dv), v, "v")
+    assert_p16_within_ulp(from_dev(dp), p_or, "p16")

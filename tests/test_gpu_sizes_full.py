@@ -227,3 +227,28 @@ def test_accumulation_and_owner_step_full_size():
     assert sum(1 for n in w.numels if n < 64) == 0 and min(w.numels) == 64
     del w
     torch.cuda.empty_cache()
+
+
+def test_per_backward_schedule_full_size():
+    """Config 5 sizes under the per-backward schedule: every microstep reduces the 16 ranks'
+    owned bf16 slices and adds the mean to the owner's fp32 accumulator; AdamW at the end."""
+    w = bench.Workload(5, 4096, 0, "per-backward")
+    sh = w.sh
+    idx = _sample(w, n_random=5_000)
+    print(f"config 5 per-backward: {sh.n_real} owned, {idx.size} sampled", flush=True)
+    w.step()
+    torch.cuda.synchronize()
+    acc = np.zeros(idx.size, dtype=np.float32)
+    for k in range(8):
+        row = [synth.values(synth.stream_key(5, synth.STREAM_MICRO, r, k), idx, synth.DIST_NORMAL, 1e-3,
+                            synth.BF16) for r in range(w.R)]
+        if k == 0:
+            acc[:] = oracle.reduce(row, synth.BF16, float(w.R))
+        else:
+            oracle.reduce_add(row, synth.BF16, float(w.R), acc)
+    loc = idx - np.uint64(sh.local_base)
+    assert_bits_equal(_gather(w.acc_owned, loc).numpy(), acc, "per-backward accumulator")
+    _check_owner(w, idx, bench.FIRST_STEP, reduced_g=acc)
+    _check_coverage(w)
+    del w
+    torch.cuda.empty_cache()

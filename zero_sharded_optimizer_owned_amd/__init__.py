@@ -190,8 +190,11 @@ def _rank_ptrs(rank_grads, base: int, last: int, name="rank_grads"):
 
 
 def zero_reduce_owned(rank_grads, begin: int, n: int, divisor: float, out, *, grad_base: int = 0,
-                      out_base: int = 0, accumulate: bool = False, check=None) -> None:
-    """out[f - out_base] = (start + sum_r rank_grads[r][f - grad_base]) / divisor, f in [begin, begin+n).
+                      out_base: int = 0, accumulate: int = 0, check=None) -> None:
+    """Rank reduce over flat indices [begin, begin+n) into ``out[f - out_base]``.
+
+    ``accumulate``: 0 ``out = sum/D``; 1 (or True) ``out = (out + sum)/D``;
+    2 ``out = out + sum/D`` (per-backward reduce-and-accumulate).
 
     ``check`` = (overflow int32[1], sumsq float64[1], workspace uint8[>=64 KiB]) device
     tensors to also compute the overflow flag and squared norm in the same pass.

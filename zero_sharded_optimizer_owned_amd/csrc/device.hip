@@ -295,7 +295,14 @@ struct ReduceArgs {
   CheckOut chk;
 };
 
-template <int DT, bool ACCUM, bool CHECK>
+// What the reduce does with the existing output (the `accumulate` argument).
+enum AccumMode : int {
+  kOverwrite = 0,      // out = sum / D
+  kStartFromOut = 1,   // out = (out + sum) / D
+  kAddMean = 2         // out = out + sum / D   (per-backward reduce, then accumulate)
+};
+
+template <int DT, int MODE, bool CHECK>
 __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs a) {
   const uint64_t f0 = a.begin, f1 = a.end;
   const uint64_t a0 = min(f1, (f0 + 7) & ~7ull);
@@ -308,8 +315,9 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs a) {
     if (t < a0 - f0) f = f0 + t;
     else if (t >= 8 && t - 8 < f1 - a1) f = a1 + (t - 8);
     if (f != ~0ull) {
-      const float start = ACCUM ? a.out[f - a.out_base] : 0.0f;
-      const float g = reduce_one<DT>(a.rs, f, start);
+      const float old = MODE != kOverwrite ? a.out[f - a.out_base] : 0.0f;
+      float g = reduce_one<DT>(a.rs, f, MODE == kStartFromOut ? old : 0.0f);
+      if (MODE == kAddMean) g = old + g;
       a.out[f - a.out_base] = g;
       if (CHECK) check_accum(g, sq, bad);
     }
@@ -322,14 +330,19 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs a) {
     const uint64_t t1 = min(n_vec, t0 + a.tile);
     for (uint64_t v = t0 + lane; v < t1; v += 64) {
       const uint64_t f[1] = {(v0 + v) * 8};
-      float s[1][8];
-      if (ACCUM) {
+      float s[1][8], old[8];
+      if (MODE == kStartFromOut) {
         load8f(a.out, f[0] - a.out_base, s[0]);
       } else {
+        if (MODE == kAddMean) load8f(a.out, f[0] - a.out_base, old);
 #pragma unroll
         for (int k = 0; k < 8; ++k) s[0][k] = 0.0f;
       }
       reduce_vec<DT, 1>(a.rs, f, s);
+      if (MODE == kAddMean) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s[0][k] = old[k] + s[0][k];
+      }
       Elem<ZERO_F32>::store8(a.out, f[0] - a.out_base, s[0]);
       if (CHECK) {
 #pragma unroll
@@ -651,15 +664,17 @@ int launch_status(const char* who) {
   return ZERO_OK;
 }
 
+template <int DT, int MODE>
+void launch_reduce_m(const ReduceArgs& a, bool check, uint32_t grid, hipStream_t s) {
+  if (check) hipLaunchKernelGGL((reduce_kernel<DT, MODE, true>), grid, kBlock, 0, s, a);
+  else hipLaunchKernelGGL((reduce_kernel<DT, MODE, false>), grid, kBlock, 0, s, a);
+}
+
 template <int DT>
-void launch_reduce(const ReduceArgs& a, bool accum, bool check, uint32_t grid, hipStream_t s) {
-  if (accum) {
-    if (check) hipLaunchKernelGGL((reduce_kernel<DT, true, true>), grid, kBlock, 0, s, a);
-    else hipLaunchKernelGGL((reduce_kernel<DT, true, false>), grid, kBlock, 0, s, a);
-  } else {
-    if (check) hipLaunchKernelGGL((reduce_kernel<DT, false, true>), grid, kBlock, 0, s, a);
-    else hipLaunchKernelGGL((reduce_kernel<DT, false, false>), grid, kBlock, 0, s, a);
-  }
+void launch_reduce(const ReduceArgs& a, int mode, bool check, uint32_t grid, hipStream_t s) {
+  if (mode == kStartFromOut) launch_reduce_m<DT, kStartFromOut>(a, check, grid, s);
+  else if (mode == kAddMean) launch_reduce_m<DT, kAddMean>(a, check, grid, s);
+  else launch_reduce_m<DT, kOverwrite>(a, check, grid, s);
 }
 
 // Blocks of `kernel` that fit on one CU at once.
@@ -727,6 +742,8 @@ extern "C" int zero_reduce_owned(const void* const* rank_grads, uint32_t R, int 
   if (out_base % 8 != 0) return fail(ZERO_EINVAL, "%s: out_base must be a multiple of 8", who);
   if (begin < out_base) return fail(ZERO_EINVAL, "%s: begin lies below out_base", who);
   if (n > UINT64_MAX - begin) return fail(ZERO_EINVAL, "%s: begin + n overflows", who);
+  if (accumulate < kOverwrite || accumulate > kAddMean)
+    return fail(ZERO_EINVAL, "%s: accumulate must be 0, 1 or 2", who);
   const bool check = d_overflow != nullptr || d_sumsq != nullptr;
   if (check) {
     if (!d_overflow || !d_sumsq)
@@ -745,9 +762,9 @@ extern "C" int zero_reduce_owned(const void* const* rank_grads, uint32_t R, int 
   const uint32_t grid = plan.grid;
   a.tile = plan.tile;
   switch (grad_dtype) {
-    case ZERO_F16: launch_reduce<ZERO_F16>(a, accumulate != 0, check, grid, stream); break;
-    case ZERO_BF16: launch_reduce<ZERO_BF16>(a, accumulate != 0, check, grid, stream); break;
-    default: launch_reduce<ZERO_F32>(a, accumulate != 0, check, grid, stream); break;
+    case ZERO_F16: launch_reduce<ZERO_F16>(a, accumulate, check, grid, stream); break;
+    case ZERO_BF16: launch_reduce<ZERO_BF16>(a, accumulate, check, grid, stream); break;
+    default: launch_reduce<ZERO_F32>(a, accumulate, check, grid, stream); break;
   }
   if ((rc = launch_status(who))) return rc;
   if (check) {
