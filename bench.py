@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--chunk", type=int, default=4096, help="max chunk elements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--op", default="step", choices=("step", "export"),
+                    help="step: the owner's optimizer step; export: copy the owner's fp32 master "
+                         "into the dense per-tensor layout (checkpoint consolidation)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB fp32 device copy (counter calibration)")
     return ap.parse_args()
@@ -398,6 +401,59 @@ def cpu_baseline(w: Workload, seconds: float):
 
 
 
+def export_bench(w: Workload, args):
+    """Time the consolidation copy of the owner's fp32 master into dense per-tensor weights."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    sh = w.sh
+    dense = torch.zeros(sh.dense_total, dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        sh.to_dense(sh.master, dense)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(args.steps):
+        sh.to_dense(sh.master, dense)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    n = sh.n_real
+    nbytes = 8 * n
+    line = {
+        "metric": "owned-shard fp32 export params/sec + achieved HBM GB/s (fraction of MI355X peak)",
+        "value": round(n / (ms / 1e3), 1), "unit": "params/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name + "; export of the owner's master to dense per-tensor fp32",
+                   "config": args.config, "op": "export", "owned_params": n},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (ms / 1e3) / 1e9, 1), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(nbytes / (ms / 1e3) / 1e9 / PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "owner_to_dense", "kernel_ms": round(ms, 4), "bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        # the oracle's plain loop over the owner's first 2^16 real elements
+        import synth
+
+        m = 1 << 16
+        first = [(int(c["flat"]), int(c["flat"]) + int(c["len"])) for c in sh.chunks[:max(1, m // 512)]]
+        lo, hi = first[0][0], first[-1][1]
+        arr = synth.values_f32(synth.stream_key(w.cfg, synth.STREAM_MASTER, 0), synth.arange(lo & ~7, hi),
+                               synth.DIST_NORMAL, 0.02)
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            numels = [b - a for a, b in first]
+            oracle.consolidate(numels, [a for a, _ in first], [(lo, hi)], [arr], [lo & ~7])
+            reps += 1
+        el = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": reps * (hi - lo) / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+                                "sample": f"{hi - lo} real elements of the owner's shard (pure-Python loop)"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -421,6 +477,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     w = Workload(args.config, args.chunk, args.grid, args.schedule)
+    if args.op == "export":
+        return export_bench(w, args)
     for _ in range(args.warmup):
         w.step()
     torch.cuda.synchronize()

@@ -261,6 +261,39 @@ typedef struct {
  * -------------------------------------------------------------------------- */
 int zero_adam_step(const zero_adam_args *args, hipStream_t stream);
 
+/* ----------------------------------------------------------------------------
+ * zero_owner_to_dense / zero_dense_to_owner -- export and import of fp32 shard
+ * data (master weights or moments) between one owner's shard and the dense
+ * per-tensor layout (every tensor's elements in order, tensors concatenated,
+ * no padding).
+ *
+ * [Deep dive] "Resume training and export weights separately": exporting a
+ * model consolidates the fp32 weights from the owners' shards; a weights-only
+ * restore loads them back with fresh moments (and resumes a different
+ * trajectory than a full-state restore).  Calling zero_owner_to_dense for
+ * every owner of a layout fills the whole dense buffer.
+ *
+ * For every real element f of the chunk table within [begin, end), in chunk
+ * c = (flat, len, k):  dense[dense_offset[k] + f - tensor_offset[k]]  <->
+ * owner[f - owner_base].
+ * chunks[n_chunks]            device: the owner's chunk table
+ * tensor_offset, dense_offset device uint64 [n_tensors]: flat and dense start of
+ *                             each tensor (dense_offset[k] = sum of numel[j<k])
+ * owner                       device fp32, at least end - owner_base elements
+ * dense                       device fp32 [dense_total]
+ * Chunks naming a tensor >= n_tensors, and dense indices >= dense_total, are
+ * skipped.  Errors: EINVAL (NULL pointers with work to do, begin > end,
+ * owner_base > begin, misaligned fp32 pointers); EHIP.
+ * -------------------------------------------------------------------------- */
+int zero_owner_to_dense(const zero_chunk *chunks, uint64_t n_chunks, uint64_t begin, uint64_t end,
+                        const uint64_t *tensor_offset, const uint64_t *dense_offset,
+                        uint32_t n_tensors, const float *owner, uint64_t owner_base, float *dense,
+                        uint64_t dense_total, hipStream_t stream);
+int zero_dense_to_owner(const zero_chunk *chunks, uint64_t n_chunks, uint64_t begin, uint64_t end,
+                        const uint64_t *tensor_offset, const uint64_t *dense_offset,
+                        uint32_t n_tensors, const float *dense, uint64_t dense_total, float *owner,
+                        uint64_t owner_base, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -181,6 +181,48 @@ def real_ranges(numels: Sequence[int], offsets: Sequence[int], begin: int, end: 
     return out
 
 
+def dense_offsets(numels: Sequence[int]) -> List[int]:
+    """Start of each tensor in the dense (unpadded) concatenation of all tensors."""
+    out, pos = [], 0
+    for n in numels:
+        out.append(pos)
+        pos += n
+    return out
+
+
+def consolidate(numels: Sequence[int], offsets: Sequence[int], owners, arrays, bases) -> np.ndarray:
+    """Dense fp32 weights from the owners' shards (export of a sharded checkpoint).
+
+    [Deep dive] "Resume training and export weights separately": exporting a
+    model consolidates the fp32 weights.  Tensor k's element j is flat index
+    ``offsets[k] + j``; it is read from the one owner whose range holds it,
+    at ``arrays[r][f - bases[r]]``.  Padding is dropped.  Plain loops.
+    """
+    out = np.empty(sum(numels), dtype=np.float32)
+    pos = 0
+    for n, off in zip(numels, offsets):
+        for j in range(n):
+            f = off + j
+            r = next(r for r, (b, e) in enumerate(owners) if b <= f < e)
+            out[pos] = arrays[r][f - bases[r]]
+            pos += 1
+    return out
+
+
+def distribute(numels: Sequence[int], offsets: Sequence[int], begin: int, end: int, dense: np.ndarray,
+               out: np.ndarray, base: int) -> np.ndarray:
+    """The inverse for one owner: write its real elements from dense weights into
+    ``out[f - base]``; padding and other elements of ``out`` are left as they are."""
+    dpos = 0
+    for n, off in zip(numels, offsets):
+        for j in range(n):
+            f = off + j
+            if begin <= f < end:
+                out[f - base] = dense[dpos + j]
+        dpos += n
+    return out
+
+
 def clip_coef(sumsq: float, max_norm: float = 1.0, eps: float = 1e-6) -> float:
     """Global-norm clip factor ``min(1, max_norm / (sqrt(sumsq) + eps))``.
 

@@ -28,7 +28,8 @@ ZERO_MAX_RANKS = 256
 ZERO_CHECK_WS_BYTES = 65536
 
 EXPORTED = ("zero_last_error", "zero_shard_layout", "zero_chunk_table", "zero_state_bytes",
-            "zero_reduce_owned", "zero_grad_check", "zero_clip_coef", "zero_adam_step")
+            "zero_reduce_owned", "zero_grad_check", "zero_clip_coef", "zero_adam_step",
+            "zero_owner_to_dense", "zero_dense_to_owner")
 
 CHUNK_DTYPE = np.dtype([("flat", "<u8"), ("len", "<u4"), ("tensor", "<u4")])
 
@@ -76,6 +77,8 @@ def load(path: str):
     L.zero_grad_check.argtypes = [P, U64, P, P, P, ct.c_size_t, P]
     L.zero_clip_coef.argtypes = [D, D, D, ct.POINTER(F)]
     L.zero_adam_step.argtypes = [ct.POINTER(AdamArgs), P]
+    L.zero_owner_to_dense.argtypes = [P, U64, U64, U64, P, P, U32, P, U64, P, U64, P]
+    L.zero_dense_to_owner.argtypes = [P, U64, U64, U64, P, P, U32, P, U64, P, U64, P]
     return L
 
 
@@ -290,6 +293,44 @@ def zero_adam_step(*, chunks_dev, n_chunks: int, begin: int, end: int, master, e
     del keep
 
 
+def _dense_call(name, chunks_dev, n_chunks, begin, end, tensor_offset_dev, dense_offset_dev, owner,
+                owner_base, dense):
+    torch = _torch()
+    _dev(owner, "owner", torch.float32)
+    _dev(dense, "dense", torch.float32)
+    _dev(tensor_offset_dev, "tensor_offset", torch.int64)
+    _dev(dense_offset_dev, "dense_offset", torch.int64)
+    if tensor_offset_dev.numel() != dense_offset_dev.numel():
+        raise ValueError("tensor and dense offset tables differ in length")
+    _need(owner, "owner", end - owner_base)
+    if chunks_dev is not None and chunks_dev.numel() * chunks_dev.element_size() < n_chunks * CHUNK_DTYPE.itemsize:
+        raise ValueError("chunk table smaller than n_chunks")
+    L = lib()
+    common = (ct.c_void_p(chunks_dev.data_ptr()) if chunks_dev is not None else None, n_chunks, begin, end,
+              ct.c_void_p(tensor_offset_dev.data_ptr()), ct.c_void_p(dense_offset_dev.data_ptr()),
+              tensor_offset_dev.numel())
+    if name == "zero_owner_to_dense":
+        _check(L.zero_owner_to_dense(*common, ct.c_void_p(owner.data_ptr()), owner_base,
+                                     ct.c_void_p(dense.data_ptr()), dense.numel(), _stream()))
+    else:
+        _check(L.zero_dense_to_owner(*common, ct.c_void_p(dense.data_ptr()), dense.numel(),
+                                     ct.c_void_p(owner.data_ptr()), owner_base, _stream()))
+
+
+def zero_owner_to_dense(chunks_dev, n_chunks, begin, end, tensor_offset_dev, dense_offset_dev, owner,
+                        owner_base, dense) -> None:
+    """dense[dense_offset[k] + f - tensor_offset[k]] = owner[f - owner_base] for the owner's real f."""
+    _dense_call("zero_owner_to_dense", chunks_dev, n_chunks, begin, end, tensor_offset_dev,
+                dense_offset_dev, owner, owner_base, dense)
+
+
+def zero_dense_to_owner(chunks_dev, n_chunks, begin, end, tensor_offset_dev, dense_offset_dev, dense,
+                        owner, owner_base) -> None:
+    """owner[f - owner_base] = dense[dense_offset[k] + f - tensor_offset[k]] for the owner's real f."""
+    _dense_call("zero_dense_to_owner", chunks_dev, n_chunks, begin, end, tensor_offset_dev,
+                dense_offset_dev, owner, owner_base, dense)
+
+
 # ---------------------------------------------------------------- convenience
 class OwnerShard:
     """One owner's layout, device chunk table and fp32 master/moment state.
@@ -312,7 +353,11 @@ class OwnerShard:
         self.device = torch.device(device or "cuda")
         self.chunks_dev = chunks_to_device(self.chunks, self.device)
         self.n_real = int(self.chunks["len"].sum()) if self.chunks.size else 0
-        self.step_count = 0
+        self.align = align
+        self.dense_total = int(sum(self.numels))
+        dense_off = np.concatenate([[0], np.cumsum(self.numels)[:-1]]).astype(np.int64)
+        self.tensor_offset_dev = torch.from_numpy(self.offsets.astype(np.int64)).to(self.device)
+        self.dense_offset_dev = torch.from_numpy(dense_off).to(self.device)
 
     def alloc_state(self):
         torch = _torch()
@@ -329,3 +374,35 @@ class OwnerShard:
                        rank_grads=rank_grads, grad_base=grad_base, divisor=divisor,
                        reduced_g=reduced_g, param16=param16, param_base=param_base,
                        clip_coef=clip_coef, grid_blocks=grid_blocks, **hyper)
+
+    # -- export / import of fp32 shard data in the dense per-tensor layout
+    def to_dense(self, owner_array, dense) -> None:
+        """Write this owner's real elements of an owner-local fp32 array into dense weights."""
+        zero_owner_to_dense(self.chunks_dev, self.chunks.size, self.begin, self.end, self.tensor_offset_dev,
+                            self.dense_offset_dev, owner_array, self.local_base, dense)
+
+    def from_dense(self, dense, owner_array) -> None:
+        """Fill this owner's real elements of an owner-local fp32 array from dense weights."""
+        zero_dense_to_owner(self.chunks_dev, self.chunks.size, self.begin, self.end, self.tensor_offset_dev,
+                            self.dense_offset_dev, dense, owner_array, self.local_base)
+
+    # -- checkpoint of the owner's optimizer state
+    def save(self, path: str, step: int) -> None:
+        """Owner checkpoint: fp32 master, both moments, the step count and the layout."""
+        np.savez(path, master=self.master.cpu().numpy(), exp_avg=self.exp_avg.cpu().numpy(),
+                 exp_avg_sq=self.exp_avg_sq.cpu().numpy(), step=np.int64(step),
+                 numels=np.array(self.numels, dtype=np.int64), ranks=np.int64(self.ranks),
+                 owner=np.int64(self.owner), align=np.int64(self.align))
+
+    def load(self, path: str) -> int:
+        """Restore a checkpoint written by save() for the same layout; returns its step."""
+        torch = _torch()
+        with np.load(path, allow_pickle=False) as z:
+            same = (list(z["numels"]) == self.numels and int(z["ranks"]) == self.ranks
+                    and int(z["owner"]) == self.owner and int(z["align"]) == self.align)
+            if not same:
+                raise ValueError("checkpoint was written for a different layout or owner")
+            self.master = torch.from_numpy(z["master"]).to(self.device)
+            self.exp_avg = torch.from_numpy(z["exp_avg"]).to(self.device)
+            self.exp_avg_sq = torch.from_numpy(z["exp_avg_sq"]).to(self.device)
+            return int(z["step"])

@@ -559,6 +559,59 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Export / import between an owner's shard and the dense per-tensor layout.
+// ---------------------------------------------------------------------------
+struct DenseArgs {
+  const zero_chunk* chunks;
+  uint64_t n_chunks;
+  uint64_t begin, end;
+  const uint64_t* tensor_offset;  // [n_tensors] flat start of each tensor
+  const uint64_t* dense_offset;   // [n_tensors] dense start of each tensor
+  uint32_t n_tensors;
+  float* owner;                   // element f - owner_base
+  uint64_t owner_base;
+  float* dense;                   // [dense_total]
+  uint64_t dense_total;
+};
+
+// Each wavefront copies whole chunks, 64 consecutive elements per instruction
+// on both sides, four instructions in flight per lane.  Chunks whose tensor
+// index or position disagrees with the tables are skipped, and no dense
+// index at or past dense_total is touched.
+template <bool TO_DENSE>
+__global__ void __launch_bounds__(kBlock) dense_kernel(const DenseArgs a) {
+  const uint64_t lane = threadIdx.x & 63;
+  const uint64_t wave =
+      __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const uint64_t n_waves = (uint64_t)gridDim.x * kWavesPerBlock;
+  for (uint64_t c = wave; c < a.n_chunks; c += n_waves) {
+    const zero_chunk ch = a.chunks[c];
+    if (ch.tensor >= a.n_tensors) continue;
+    const uint64_t toff = a.tensor_offset[ch.tensor];
+    const uint64_t doff = a.dense_offset[ch.tensor];
+    const uint64_t f0 = max(max(ch.flat, a.begin), toff);
+    const uint64_t f1 = min(ch.flat + ch.len, a.end);
+    for (uint64_t f = f0 + lane; f < f1; f += 256) {
+      float x[4];
+      uint64_t d[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint64_t fj = f + 64 * j;
+        d[j] = fj < f1 ? doff + (fj - toff) : a.dense_total;
+        if (d[j] < a.dense_total) x[j] = TO_DENSE ? a.owner[fj - a.owner_base] : a.dense[d[j]];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (d[j] < a.dense_total) {
+          if (TO_DENSE) a.dense[d[j]] = x[j];
+          else a.owner[f + 64 * j - a.owner_base] = x[j];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side planning and validation.
 // ---------------------------------------------------------------------------
 constexpr int kMaxDevices = 64;
@@ -875,4 +928,66 @@ extern "C" int zero_adam_step(const zero_adam_args* p, hipStream_t stream) {
     }
   }
   return launch_status(who);
+}
+
+namespace {
+int dense_copy(bool to_dense, const zero_chunk* chunks, uint64_t n_chunks, uint64_t begin,
+               uint64_t end, const uint64_t* tensor_offset, const uint64_t* dense_offset,
+               uint32_t n_tensors, float* owner, uint64_t owner_base, float* dense,
+               uint64_t dense_total, hipStream_t stream, const char* who) {
+  clear_error();
+  if (begin > end) return fail(ZERO_EINVAL, "%s: begin > end", who);
+  if (n_chunks > 0 && (!chunks || !tensor_offset || !dense_offset || !owner || !dense))
+    return fail(ZERO_EINVAL, "%s: NULL pointer argument", who);
+  if (n_tensors == 0 && n_chunks > 0) return fail(ZERO_EINVAL, "%s: no tensors", who);
+  if (owner_base > begin) return fail(ZERO_EINVAL, "%s: owner_base lies above begin", who);
+  if ((reinterpret_cast<uintptr_t>(owner) | reinterpret_cast<uintptr_t>(dense)) & 3u)
+    return fail(ZERO_EINVAL, "%s: fp32 buffers must be 4-byte aligned", who);
+  if (n_chunks == 0 || begin == end) return ZERO_OK;
+  int cus = 0;
+  int rc = cu_count(&cus);
+  if (rc) return rc;
+  DenseArgs a;
+  a.chunks = chunks;
+  a.n_chunks = n_chunks;
+  a.begin = begin;
+  a.end = end;
+  a.tensor_offset = tensor_offset;
+  a.dense_offset = dense_offset;
+  a.n_tensors = n_tensors;
+  a.owner = owner;
+  a.owner_base = owner_base;
+  a.dense = dense;
+  a.dense_total = dense_total;
+  if (to_dense) {
+    static const uint32_t per_cu = blocks_per_cu(dense_kernel<true>);
+    hipLaunchKernelGGL(dense_kernel<true>, persistent_grid(per_cu, n_chunks, cus, 0), kBlock, 0,
+                       stream, a);
+  } else {
+    static const uint32_t per_cu = blocks_per_cu(dense_kernel<false>);
+    hipLaunchKernelGGL(dense_kernel<false>, persistent_grid(per_cu, n_chunks, cus, 0), kBlock, 0,
+                       stream, a);
+  }
+  return launch_status(who);
+}
+}  // namespace
+
+extern "C" int zero_owner_to_dense(const zero_chunk* chunks, uint64_t n_chunks, uint64_t begin,
+                                   uint64_t end, const uint64_t* tensor_offset,
+                                   const uint64_t* dense_offset, uint32_t n_tensors,
+                                   const float* owner, uint64_t owner_base, float* dense,
+                                   uint64_t dense_total, hipStream_t stream) {
+  return dense_copy(true, chunks, n_chunks, begin, end, tensor_offset, dense_offset, n_tensors,
+                    const_cast<float*>(owner), owner_base, dense, dense_total, stream,
+                    "zero_owner_to_dense");
+}
+
+extern "C" int zero_dense_to_owner(const zero_chunk* chunks, uint64_t n_chunks, uint64_t begin,
+                                   uint64_t end, const uint64_t* tensor_offset,
+                                   const uint64_t* dense_offset, uint32_t n_tensors,
+                                   const float* dense, uint64_t dense_total, float* owner,
+                                   uint64_t owner_base, hipStream_t stream) {
+  return dense_copy(false, chunks, n_chunks, begin, end, tensor_offset, dense_offset, n_tensors,
+                    owner, owner_base, const_cast<float*>(dense), dense_total, stream,
+                    "zero_dense_to_owner");
 }
