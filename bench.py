@@ -49,17 +49,23 @@ def parse():
     ap.add_argument("--chunk", type=int, default=4096, help="max chunk elements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--op", default="step", choices=("step", "export"),
+    ap.add_argument("--op", default="step", choices=("step", "export", "gather3"),
                     help="step: the owner's optimizer step; export: copy the owner's fp32 master "
-                         "into the dense per-tensor layout (checkpoint consolidation)")
+                         "into the dense per-tensor layout (checkpoint consolidation); gather3: the "
+                         "ZeRO-3 gather of four Llama-style layers from 8 ranks' bf16 shard buffers")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB fp32 device copy (counter calibration)")
     return ap.parse_args()
 
 
 def kernel_source_hash() -> str:
-    p = os.path.join(ROOT, "zero_sharded_optimizer_owned_amd", "csrc", "device.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Hash of the sources of the step kernels (counter records are tied to it)."""
+    from zero_sharded_optimizer_owned_amd.build import CSRC, STEP_SOURCES
+
+    h = hashlib.sha256()
+    for name in STEP_SOURCES:
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_record(name: str):
@@ -401,6 +407,112 @@ def cpu_baseline(w: Workload, seconds: float):
 
 
 
+class Stage3Gather:
+    """ZeRO-3 working set: the first four layers (36 tensors) of the Llama-style list,
+    gathered from 8 ranks' bf16 shard buffers (each holds its ceil(n/8) shard of all
+    289 tensors) into full padded buffers."""
+
+    SEED = 6
+
+    def __init__(self, n_layers: int = 4, R: int = 8):
+        import numpy as np
+        import torch
+
+        import synth
+        import zero_sharded_optimizer_owned_amd as zs
+
+        self.numels, self.R = llama_numels(), R
+        self.live = list(range(1, 1 + 9 * n_layers))
+        self.shard_numel, self.resident, self.gathered = zs.zero3_storage(self.numels, R, self.live)
+        self.shards = []
+        for r in range(R):
+            t = torch.empty(self.resident, dtype=torch.bfloat16, device="cuda")
+            fill(t, self.SEED, synth.STREAM_MASTER, r, 0, synth.DIST_NORMAL, 0.02)
+            self.shards.append(t)
+        self.out = torch.empty(self.gathered, dtype=torch.bfloat16, device="cuda")
+        self.spans = zs.zero3_gather_spans(self.numels, R, self.live, max_span=1 << 16)
+        self.spans_dev = zs.spans_to_device(self.spans)
+        self.so = np.concatenate([[0], np.cumsum(self.shard_numel)[:-1]]).astype(np.int64)
+        torch.cuda.synchronize()
+
+    def run(self):
+        import zero_sharded_optimizer_owned_amd as zs
+
+        zs.zero_copy_spans(self.spans_dev, self.spans.size, self.shards, self.out)
+
+    def expected(self, pos):
+        """Generator values at gather-buffer positions (rank r's shard element so_k + j)."""
+        import numpy as np
+
+        import synth
+
+        want = np.empty(pos.size, dtype=np.uint16)
+        base = 0
+        for k in self.live:
+            s = int(self.shard_numel[k])
+            sel = (pos >= base) & (pos < base + self.R * s)
+            rel = pos[sel] - base
+            r, j = rel // s, rel % s
+            for rr in np.unique(r):
+                m = r == rr
+                idx = (self.so[k] + j[m]).astype(np.uint64)
+                vals = synth.values(synth.stream_key(self.SEED, synth.STREAM_MASTER, int(rr)), idx,
+                                    synth.DIST_NORMAL, 0.02, synth.BF16)
+                tmp = want[sel]
+                tmp[m] = vals
+                want[sel] = tmp
+            base += self.R * s
+        return want
+
+
+def gather3_bench(args):
+    import torch
+
+    g = Stage3Gather()
+    for _ in range(args.warmup):
+        g.run()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(args.steps):
+        g.run()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    nbytes = 4 * g.gathered  # each bf16 element read once and written once
+    line = {
+        "metric": "ZeRO-3 gathered params/sec + achieved HBM GB/s (fraction of MI355X peak)",
+        "value": round(g.gathered / (ms / 1e3), 1), "unit": "params/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Llama-style list (289 tensors), R=8 per-tensor shards, gather of layers 0-3 "
+                               "(36 tensors) into full padded buffers", "op": "gather3",
+                   "gathered_params": g.gathered, "resident_per_rank": g.resident, "spans": int(g.spans.size)},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (ms / 1e3) / 1e9, 1), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(nbytes / (ms / 1e3) / 1e9 / PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "span_kernel<uint16_t>", "kernel_ms": round(ms, 4), "bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+
+        import oracle
+        import synth
+
+        # the oracle's plain loops on a small model of the same shape (R=8, 9 tensors of one layer / 64)
+        sizes = [n // 64 for n in llama_numels()[1:10]]
+        dense = synth.values_f32(synth.stream_key(6, synth.STREAM_MASTER, 0), synth.arange(0, sum(sizes)),
+                                 synth.DIST_NORMAL, 0.02)
+        t0 = time.perf_counter()
+        shards = oracle.stage3_shards(sizes, 8, dense)
+        t1 = time.perf_counter()
+        outg = oracle.stage3_gather(sizes, 8, shards, list(range(len(sizes))))
+        t2 = time.perf_counter()
+        line["cpu_baseline"] = {"value": outg.size / (t2 - t1), "unit": "params/s", "cores": 1, "kind": "oracle",
+                                "sample": f"gather of one layer scaled by 1/64 ({outg.size} elements; "
+                                          f"partition loop {t1 - t0:.1f} s untimed)"}
+    print(json.dumps(line), flush=True)
+
+
 def export_bench(w: Workload, args):
     """Time the consolidation copy of the owner's fp32 master into dense per-tensor weights."""
     import numpy as np
@@ -468,6 +580,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     zs.lib()
+    if args.op == "gather3":
+        return gather3_bench(args)
     if args.calibrate_copy:
         # a plain copy of known size: 2^28 fp32 read + 2^28 fp32 written per launch
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")

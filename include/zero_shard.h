@@ -294,6 +294,68 @@ int zero_dense_to_owner(const zero_chunk *chunks, uint64_t n_chunks, uint64_t be
                         uint32_t n_tensors, const float *dense, uint64_t dense_total, float *owner,
                         uint64_t owner_base, hipStream_t stream);
 
+/* ----------------------------------------------------------------------------
+ * ZeRO-3 per-tensor partitioning and the gathered working set.
+ *
+ * [Deep dive] "Stage 3 needs a live working set": each tensor k of n_k
+ * elements is cut into R shards of s_k = ceil(n_k / R) elements (rank r holds
+ * elements [r s_k, (r+1) s_k), zero past the end of the tensor).  A rank's
+ * shard buffer holds its shards of all tensors in tensor order (tensor k at
+ * so_k = sum of s_j, j < k).  Using a tensor gathers all R shards into a
+ * separate full buffer of R s_k elements, in rank order; the tensor is its
+ * first n_k elements.  Live tensors' buffers follow each other in the order
+ * the live list gives.
+ *
+ * zero3_storage: resident = sum_k s_k elements per rank, gathered = sum over
+ *   live tensors of R s_k; shard_numel[k] = s_k (shard_numel may be NULL).
+ * zero3_gather_spans: the copy spans that assemble the live tensors' buffers
+ *   from the R shard buffers (span.buf = source rank).
+ * zero3_partition_spans: the copy spans that cut rank `rank`'s shard buffer
+ *   out of the dense tensors (tensors concatenated, no padding); the padding
+ *   past each tensor's end is not written, so the shard buffer should start
+ *   zeroed.
+ * Span tables follow zero_chunk_table's conventions: spans of at most
+ * max_span elements; out == NULL with capacity == 0 only counts; ERANGE when
+ * capacity is short (the first `capacity` spans are written).
+ * Errors: EINVAL for ranks 0, a 0-element tensor, a live index out of range
+ * or listed twice, rank >= ranks, max_span 0; ERANGE for counts above 2^64.
+ * -------------------------------------------------------------------------- */
+typedef struct {
+  uint64_t src;  /* first element in source buffer `buf` */
+  uint64_t dst;  /* first element in the destination */
+  uint32_t len;  /* elements */
+  uint32_t buf;  /* source buffer index */
+} zero_copy_span;
+
+int zero3_storage(const uint64_t *numel, uint32_t n_tensors, uint32_t ranks, const uint32_t *live,
+                  uint32_t n_live, uint64_t *shard_numel, uint64_t *resident, uint64_t *gathered);
+int zero3_gather_spans(const uint64_t *numel, uint32_t n_tensors, uint32_t ranks,
+                       const uint32_t *live, uint32_t n_live, uint32_t max_span,
+                       zero_copy_span *out, uint64_t capacity, uint64_t *n_spans);
+int zero3_partition_spans(const uint64_t *numel, uint32_t n_tensors, uint32_t ranks,
+                          uint32_t rank, uint32_t max_span, zero_copy_span *out,
+                          uint64_t capacity, uint64_t *n_spans);
+
+/* Most source buffers one zero_copy_spans call can read. */
+#define ZERO_MAX_COPY_SOURCES 128
+
+/* ----------------------------------------------------------------------------
+ * zero_copy_spans -- dst[span.dst + i] = srcs[span.buf][span.src + i] for every
+ * span of a device span table, in one persistent multi-span launch.  The
+ * device side of the stage-3 gather (and partition) on one GPU.
+ * spans[n_spans]      device table (from the builders above)
+ * srcs, src_numel     host arrays [n_srcs] of device pointers and their
+ *                     element counts; n_srcs <= ZERO_MAX_COPY_SOURCES
+ * dst, dst_numel      device destination and its element count
+ * elem_bytes          2 (fp16/bf16) or 4 (fp32)
+ * Spans whose buffer index or extent falls outside these counts are skipped.
+ * Errors: EINVAL (NULL pointers with work, bad elem_bytes, n_srcs out of
+ * range, pointers not 16-byte aligned); EHIP.
+ * -------------------------------------------------------------------------- */
+int zero_copy_spans(const zero_copy_span *spans, uint64_t n_spans, const void *const *srcs,
+                    const uint64_t *src_numel, uint32_t n_srcs, void *dst, uint64_t dst_numel,
+                    uint32_t elem_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

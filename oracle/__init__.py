@@ -148,6 +148,43 @@ def parameter_storage(layer_sizes: Sequence[int], ranks: int, live_layers: Seque
     return resident, gathered, resident + gathered
 
 
+def stage3_shards(layer_sizes: Sequence[int], ranks: int, dense: np.ndarray) -> List[np.ndarray]:
+    """Every rank's shard buffer under per-tensor ZeRO-3 partitioning.
+
+    [Deep dive] "Stage 3 needs a live working set": tensor k is cut into
+    ranks shards of ceil(n_k / ranks) elements; rank r holds elements
+    [r*s_k, (r+1)*s_k) of it, zero past the tensor's end.  A rank's buffer
+    holds its shards of all tensors in tensor order.  ``dense`` is the
+    tensors' elements concatenated.  Plain loops.
+    """
+    shards = [-(-n // ranks) for n in layer_sizes]
+    out = [np.zeros(sum(shards), dtype=dense.dtype) for _ in range(ranks)]
+    for r in range(ranks):
+        pos, dpos = 0, 0
+        for n, s in zip(layer_sizes, shards):
+            for j in range(s):
+                e = r * s + j
+                if e < n:
+                    out[r][pos + j] = dense[dpos + e]
+            pos += s
+            dpos += n
+    return out
+
+
+def stage3_gather(layer_sizes: Sequence[int], ranks: int, shard_buffers: Sequence[np.ndarray],
+                  live: Sequence[int]) -> np.ndarray:
+    """The gathered working set: for each live tensor, in the order given, a
+    separate full buffer of ranks * ceil(n / ranks) elements holding the
+    ranks' shards in rank order (the tensor is its first n elements)."""
+    shards = [-(-n // ranks) for n in layer_sizes]
+    starts = [sum(shards[:k]) for k in range(len(shards))]
+    parts = []
+    for k in live:
+        for r in range(ranks):
+            parts.append(shard_buffers[r][starts[k]:starts[k] + shards[k]])
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=shard_buffers[0].dtype)
+
+
 # ---------------------------------------------------------------------------
 # Flattened, padded parameter buffer (reading: the pages leave padding open).
 # ---------------------------------------------------------------------------

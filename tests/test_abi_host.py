@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "ze
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(zero_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(zero\d*_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -171,3 +171,56 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
                                ct.c_void_p(0x4000), ct.c_void_p(0x10000), 100,
                                None) == zs.ZERO_EINVAL  # workspace too small
     assert L.zero_grad_check(None, 0, None, None, None, 0, None) == zs.ZERO_EINVAL
+
+
+def test_stage3_storage_matches_oracle_and_printed_example():
+    import os
+
+    gold = os.path.join(os.path.dirname(__file__), "golden", "parameter_storage.txt")
+    for ln in open(gold):
+        if not ln.strip() or ln.startswith("#"):
+            continue
+        sizes_s, live_s, counts = [x.strip() for x in ln.split("|")]
+        sizes = [int(x) for x in sizes_s.split(",")]
+        live = [] if live_s == "-" else [int(x) for x in live_s.split(",")]
+        _, res, gat = zs.zero3_storage(sizes, 4, live)
+        assert (res, gat, res + gat) == tuple(int(x) for x in counts.split())
+    rnd = random.Random(5)
+    for _ in range(200):
+        sizes = [rnd.randrange(1, 10_000) for _ in range(rnd.randrange(1, 9))]
+        R = rnd.randrange(1, 70)
+        live = rnd.sample(range(len(sizes)), rnd.randrange(0, len(sizes) + 1))
+        shard, res, gat = zs.zero3_storage(sizes, R, live)
+        assert (res, gat, res + gat) == oracle.parameter_storage(sizes, R, live)
+        assert list(shard) == [-(-n // R) for n in sizes]
+    for bad in (([8, 8], 0, []), ([8, 0], 4, []), ([8], 4, [1]), ([8, 8], 4, [0, 0])):
+        with pytest.raises(zs.ZeroShardError):
+            zs.zero3_storage(*bad)
+
+
+def _apply_spans(spans, srcs, dst):
+    for sp in spans:
+        s, d, n, b = int(sp["src"]), int(sp["dst"]), int(sp["len"]), int(sp["buf"])
+        dst[d:d + n] = srcs[b][s:s + n]
+
+
+def test_stage3_span_tables_reproduce_the_oracle():
+    rnd = random.Random(6)
+    rng = np.random.default_rng(6)
+    for _ in range(60):
+        sizes = [rnd.randrange(1, 300) for _ in range(rnd.randrange(1, 7))]
+        R = rnd.randrange(1, 9)
+        dense = rng.standard_normal(sum(sizes)).astype(np.float32)
+        shards = oracle.stage3_shards(sizes, R, dense)
+        for r in range(R):
+            out = np.zeros_like(shards[r])
+            _apply_spans(zs.zero3_partition_spans(sizes, R, r, max_span=rnd.choice([1, 7, 64, 1 << 16])),
+                         [dense], out)
+            assert np.array_equal(out, shards[r])
+        live = rnd.sample(range(len(sizes)), rnd.randrange(0, len(sizes) + 1))
+        want = oracle.stage3_gather(sizes, R, shards, live)
+        got = np.full(want.size, np.nan, dtype=np.float32)
+        spans = zs.zero3_gather_spans(sizes, R, live, max_span=rnd.choice([3, 64, 1 << 16]))
+        assert all(int(s["len"]) >= 1 for s in spans)
+        _apply_spans(spans, shards, got)
+        assert np.array_equal(got, want)

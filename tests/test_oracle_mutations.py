@@ -91,7 +91,7 @@ PY_PROBES = [
     SB.test_printed_table_1p5e9_4_ranks, SB.test_printed_asserts, SB.test_memory_matrix_identity,
     SB.test_parameter_storage_printed, PG.test_first_step_python_and_c, PG.test_sharded_equals_unsharded_lab,
     PG.test_resume_lab_printed_values, PG.test_mean_of_squares_is_not_square_of_mean,
-    A.test_grad_check_closed_forms,
+    A.test_grad_check_closed_forms, SB.test_stage3_gather_sizes_match_parameter_storage_and_rebuild_tensors,
 ]
 
 PY_MUTANTS = {
@@ -108,6 +108,8 @@ PY_MUTANTS = {
                                 "shards = [n // ranks for n in layer_sizes]"),
     "clip never clamps": ("clip_coef", "return min(1.0, max_norm / (math.sqrt(sumsq) + eps))",
                           "return max_norm / (math.sqrt(sumsq) + eps)"),
+    "stage-3 shard starts at the floor split": ("stage3_shards", "e = r * s + j", "e = r * n // ranks + j"),
+    "stage-3 gather in tensor order": ("stage3_gather", "for k in live:", "for k in sorted(live):"),
 }
 
 

@@ -71,3 +71,26 @@ def test_parameter_storage_printed():
 def test_parameter_storage_rejects(args):
     with pytest.raises(ValueError):
         oracle.parameter_storage(*args)
+
+
+def test_stage3_gather_sizes_match_parameter_storage_and_rebuild_tensors():
+    """The gathered buffers of the live tensors have the storage counts of the
+    pages' example, and their first n elements are the tensors themselves."""
+    import numpy as np
+
+    rng = np.random.default_rng(4)
+    for sizes, R, live in ([[8, 8, 8, 8], 4, [0]], [[8, 8, 8, 8], 4, [0, 1]], [[5, 9, 2], 4, [1]],
+                           [[13, 1, 64, 7], 3, [3, 0, 2]]):
+        dense = rng.standard_normal(sum(sizes)).astype(np.float32)
+        bufs = oracle.stage3_shards(sizes, R, dense)
+        resident, gathered, total = oracle.parameter_storage(sizes, R, live)
+        assert all(b.size == resident for b in bufs)
+        g = oracle.stage3_gather(sizes, R, bufs, live)
+        assert g.size == gathered
+        dstart = [sum(sizes[:k]) for k in range(len(sizes))]
+        pos = 0
+        for k in live:
+            s = -(-sizes[k] // R)
+            assert np.array_equal(g[pos:pos + sizes[k]], dense[dstart[k]:dstart[k] + sizes[k]])
+            assert np.all(g[pos + sizes[k]:pos + R * s] == 0)  # padding of the last shards
+            pos += R * s

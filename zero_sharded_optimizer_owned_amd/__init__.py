@@ -1,7 +1,8 @@
 """ZeRO owner-shard optimizer step on one MI355X: Python binding of libzero_shard.so.
 
 Argument marshalling only.  Every step of the path runs in the HIP library
-(``csrc/device.hip``, ``csrc/host.cpp``; C ABI in ``include/zero_shard.h``);
+(``csrc/step.hip``, ``csrc/copy.hip``, ``csrc/launch.hip``, ``csrc/host.cpp``; C ABI in
+``include/zero_shard.h``);
 this module turns torch tensors into pointers, checks devices, dtypes,
 contiguity and extents against what the kernels will touch, passes torch's
 current stream, and raises on error codes.  There is no fallback: if the
@@ -29,9 +30,12 @@ ZERO_CHECK_WS_BYTES = 65536
 
 EXPORTED = ("zero_last_error", "zero_shard_layout", "zero_chunk_table", "zero_state_bytes",
             "zero_reduce_owned", "zero_grad_check", "zero_clip_coef", "zero_adam_step",
-            "zero_owner_to_dense", "zero_dense_to_owner")
+            "zero_owner_to_dense", "zero_dense_to_owner", "zero3_storage", "zero3_gather_spans",
+            "zero3_partition_spans", "zero_copy_spans")
 
 CHUNK_DTYPE = np.dtype([("flat", "<u8"), ("len", "<u4"), ("tensor", "<u4")])
+SPAN_DTYPE = np.dtype([("src", "<u8"), ("dst", "<u8"), ("len", "<u4"), ("buf", "<u4")])
+ZERO_MAX_COPY_SOURCES = 128
 
 
 class ZeroShardError(RuntimeError):
@@ -79,6 +83,10 @@ def load(path: str):
     L.zero_adam_step.argtypes = [ct.POINTER(AdamArgs), P]
     L.zero_owner_to_dense.argtypes = [P, U64, U64, U64, P, P, U32, P, U64, P, U64, P]
     L.zero_dense_to_owner.argtypes = [P, U64, U64, U64, P, P, U32, P, U64, P, U64, P]
+    L.zero3_storage.argtypes = [P, U32, U32, P, U32, P, P, P]
+    L.zero3_gather_spans.argtypes = [P, U32, U32, P, U32, U32, P, U64, P]
+    L.zero3_partition_spans.argtypes = [P, U32, U32, U32, U32, P, U64, P]
+    L.zero_copy_spans.argtypes = [P, U64, P, P, U32, P, U64, U32, P]
     return L
 
 
@@ -329,6 +337,66 @@ def zero_dense_to_owner(chunks_dev, n_chunks, begin, end, tensor_offset_dev, den
     """owner[f - owner_base] = dense[dense_offset[k] + f - tensor_offset[k]] for the owner's real f."""
     _dense_call("zero_dense_to_owner", chunks_dev, n_chunks, begin, end, tensor_offset_dev,
                 dense_offset_dev, owner, owner_base, dense)
+
+
+# ---------------------------------------------------------------- ZeRO-3 partition / gather
+def _live(live):
+    return np.ascontiguousarray(np.asarray(list(live), dtype=np.uint32))
+
+
+def zero3_storage(numels: Sequence[int], ranks: int, live: Sequence[int] = ()):
+    """(shard sizes, resident, gathered) element counts of per-tensor ZeRO-3 partitioning."""
+    n, lv = _u64(numels), _live(live)
+    shard = np.zeros(max(1, n.size), dtype=np.uint64)
+    res, gat = np.zeros(1, dtype=np.uint64), np.zeros(1, dtype=np.uint64)
+    _check(lib().zero3_storage(_p(n), n.size, ranks, _p(lv), lv.size, _p(shard), _p(res), _p(gat)))
+    return shard[: n.size], int(res[0]), int(gat[0])
+
+
+def _spans(fn, *args, max_span):
+    count = np.zeros(1, dtype=np.uint64)
+    _check(fn(*args, max_span, None, 0, _p(count)))
+    out = np.zeros(int(count[0]), dtype=SPAN_DTYPE)
+    _check(fn(*args, max_span, _p(out) if out.size else None, out.size, _p(count)))
+    return out
+
+
+def zero3_gather_spans(numels, ranks: int, live, max_span: int = 1 << 16) -> np.ndarray:
+    n, lv = _u64(numels), _live(live)
+    return _spans(lib().zero3_gather_spans, _p(n), n.size, ranks, _p(lv), lv.size, max_span=max_span)
+
+
+def zero3_partition_spans(numels, ranks: int, rank: int, max_span: int = 1 << 16) -> np.ndarray:
+    n = _u64(numels)
+    return _spans(lib().zero3_partition_spans, _p(n), n.size, ranks, rank, max_span=max_span)
+
+
+def spans_to_device(spans: np.ndarray, device=None):
+    torch = _torch()
+    return torch.from_numpy(np.ascontiguousarray(spans).view(np.uint8).copy()).to(device or "cuda")
+
+
+def zero_copy_spans(spans_dev, n_spans: int, srcs, dst) -> None:
+    """dst[span.dst + i] = srcs[span.buf][span.src + i] over a device span table."""
+    torch = _torch()
+    if not srcs or len(srcs) > ZERO_MAX_COPY_SOURCES:
+        raise ValueError(f"between 1 and {ZERO_MAX_COPY_SOURCES} source buffers")
+    _dev(dst, "dst")
+    if dst.element_size() not in (2, 4):
+        raise TypeError("elements must be 2 or 4 bytes")
+    arr = (ct.c_void_p * len(srcs))()
+    sizes = np.zeros(len(srcs), dtype=np.uint64)
+    for i, t in enumerate(srcs):
+        _dev(t, f"srcs[{i}]", dst.dtype)
+        arr[i] = t.data_ptr()
+        sizes[i] = t.numel()
+    if spans_dev is not None:
+        _dev(spans_dev, "spans")
+        if spans_dev.numel() * spans_dev.element_size() < n_spans * SPAN_DTYPE.itemsize:
+            raise ValueError("span table smaller than n_spans")
+    _check(lib().zero_copy_spans(ct.c_void_p(spans_dev.data_ptr()) if spans_dev is not None else None,
+                                 n_spans, arr, _p(sizes), len(srcs), ct.c_void_p(dst.data_ptr()),
+                                 dst.numel(), dst.element_size(), _stream()))
 
 
 # ---------------------------------------------------------------- convenience

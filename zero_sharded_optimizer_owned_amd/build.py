@@ -7,6 +7,10 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libzero_shard.so")
+SOURCES = ("host.cpp", "launch.hip", "step.hip", "copy.hip")
+# The sources whose kernels make up the optimizer step (hashed to tie counter
+# records to the code they were taken on).
+STEP_SOURCES = ("step.hip", "launch.hip", "launch.h", "internal.h")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 HIPCC_FLAGS = [
@@ -22,7 +26,7 @@ HIPCC_FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, "host.cpp"), os.path.join(CSRC, "device.hip")]
+    srcs = [os.path.join(CSRC, f) for f in SOURCES]
     tmp = LIB_PATH + ".tmp"
     cmd = ["hipcc", *HIPCC_FLAGS, "-I", INCLUDE, *srcs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

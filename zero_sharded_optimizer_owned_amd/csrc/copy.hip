@@ -1,0 +1,238 @@
+// Copy kernels of libzero_shard and their C entry points:
+//   * export and import of fp32 shard data between an owner's shard and the
+//     dense per-tensor layout (over the owner's chunk table);
+//   * span-table copies: the stage-3 gather of a live working set from the
+//     ranks' shard buffers, and the partition of dense tensors into a shard.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "internal.h"
+#include "launch.h"
+
+namespace zs {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Export / import between an owner's shard and the dense per-tensor layout.
+// ---------------------------------------------------------------------------
+struct DenseArgs {
+  const zero_chunk* chunks;
+  uint64_t n_chunks;
+  uint64_t begin, end;
+  const uint64_t* tensor_offset;  // [n_tensors] flat start of each tensor
+  const uint64_t* dense_offset;   // [n_tensors] dense start of each tensor
+  uint32_t n_tensors;
+  float* owner;                   // element f - owner_base
+  uint64_t owner_base;
+  float* dense;                   // [dense_total]
+  uint64_t dense_total;
+};
+
+// Each wavefront copies whole chunks, 64 consecutive elements per instruction
+// on both sides, four instructions in flight per lane.  Chunks whose tensor
+// index or position disagrees with the tables are skipped, and no dense
+// index at or past dense_total is touched.
+template <bool TO_DENSE>
+__global__ void __launch_bounds__(kBlock) dense_kernel(const DenseArgs a) {
+  const uint64_t lane = threadIdx.x & 63;
+  const uint64_t wave =
+      __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const uint64_t n_waves = (uint64_t)gridDim.x * kWavesPerBlock;
+  for (uint64_t c = wave; c < a.n_chunks; c += n_waves) {
+    const zero_chunk ch = a.chunks[c];
+    if (ch.tensor >= a.n_tensors) continue;
+    const uint64_t toff = a.tensor_offset[ch.tensor];
+    const uint64_t doff = a.dense_offset[ch.tensor];
+    const uint64_t f0 = max(max(ch.flat, a.begin), toff);
+    const uint64_t f1 = min(ch.flat + ch.len, a.end);
+    for (uint64_t f = f0 + lane; f < f1; f += 256) {
+      float x[4];
+      uint64_t d[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint64_t fj = f + 64 * j;
+        d[j] = fj < f1 ? doff + (fj - toff) : a.dense_total;
+        if (d[j] < a.dense_total) x[j] = TO_DENSE ? a.owner[fj - a.owner_base] : a.dense[d[j]];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (d[j] < a.dense_total) {
+          if (TO_DENSE) a.dense[d[j]] = x[j];
+          else a.owner[f + 64 * j - a.owner_base] = x[j];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Span-table copies.
+// ---------------------------------------------------------------------------
+struct SpanArgs {
+  const zero_copy_span* spans;
+  uint64_t n_spans;
+  const void* src[ZERO_MAX_COPY_SOURCES];
+  uint64_t src_numel[ZERO_MAX_COPY_SOURCES];
+  uint32_t n_srcs;
+  void* dst;
+  uint64_t dst_numel;
+};
+
+// One wavefront per span (grid stride over the table).  When source and
+// destination share their phase within a 16-byte vector, the body moves as
+// 128-bit vectors (four per lane in flight) between scalar head and tail
+// pieces; otherwise lanes copy single elements, four per lane in flight.
+// Spans that do not fit their buffers are skipped.
+template <typename T>
+__global__ void __launch_bounds__(kBlock) span_kernel(const SpanArgs a) {
+  constexpr uint64_t V = 16 / sizeof(T);
+  const uint64_t lane = threadIdx.x & 63;
+  const uint64_t wave =
+      __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const uint64_t n_waves = (uint64_t)gridDim.x * kWavesPerBlock;
+  for (uint64_t c = wave; c < a.n_spans; c += n_waves) {
+    const zero_copy_span sp = a.spans[c];
+    if (sp.buf >= a.n_srcs) continue;
+    const uint64_t len = sp.len;
+    const uint64_t sn = a.src_numel[sp.buf];
+    if (sp.src > sn || len > sn - sp.src || sp.dst > a.dst_numel || len > a.dst_numel - sp.dst) continue;
+    const T* s = static_cast<const T*>(a.src[sp.buf]) + sp.src;
+    T* d = static_cast<T*>(a.dst) + sp.dst;
+    if ((sp.src - sp.dst) % V == 0) {
+      const uint64_t head = min(len, (V - sp.dst % V) % V);
+      const uint64_t body = (len - head) / V;
+      const uint64_t tail0 = head + body * V;
+      if (lane < head) d[lane] = s[lane];
+      if (lane < len - tail0) d[tail0 + lane] = s[tail0 + lane];
+      const uint4* sv = reinterpret_cast<const uint4*>(s + head);
+      uint4* dv = reinterpret_cast<uint4*>(d + head);
+      for (uint64_t v = lane; v < body; v += 256) {
+        uint4 x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (v + 64 * j < body) x[j] = sv[v + 64 * j];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (v + 64 * j < body) dv[v + 64 * j] = x[j];
+      }
+    } else {
+      for (uint64_t i = lane; i < len; i += 256) {
+        T x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (i + 64 * j < len) x[j] = s[i + 64 * j];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (i + 64 * j < len) d[i + 64 * j] = x[j];
+      }
+    }
+  }
+}
+
+}  // namespace
+}  // namespace zs
+
+using namespace zs;
+
+namespace {
+int dense_copy(bool to_dense, const zero_chunk* chunks, uint64_t n_chunks, uint64_t begin,
+               uint64_t end, const uint64_t* tensor_offset, const uint64_t* dense_offset,
+               uint32_t n_tensors, float* owner, uint64_t owner_base, float* dense,
+               uint64_t dense_total, hipStream_t stream, const char* who) {
+  clear_error();
+  if (begin > end) return fail(ZERO_EINVAL, "%s: begin > end", who);
+  if (n_chunks > 0 && (!chunks || !tensor_offset || !dense_offset || !owner || !dense))
+    return fail(ZERO_EINVAL, "%s: NULL pointer argument", who);
+  if (n_tensors == 0 && n_chunks > 0) return fail(ZERO_EINVAL, "%s: no tensors", who);
+  if (owner_base > begin) return fail(ZERO_EINVAL, "%s: owner_base lies above begin", who);
+  if ((reinterpret_cast<uintptr_t>(owner) | reinterpret_cast<uintptr_t>(dense)) & 3u)
+    return fail(ZERO_EINVAL, "%s: fp32 buffers must be 4-byte aligned", who);
+  if (n_chunks == 0 || begin == end) return ZERO_OK;
+  int cus = 0;
+  int rc = cu_count(&cus);
+  if (rc) return rc;
+  DenseArgs a;
+  a.chunks = chunks;
+  a.n_chunks = n_chunks;
+  a.begin = begin;
+  a.end = end;
+  a.tensor_offset = tensor_offset;
+  a.dense_offset = dense_offset;
+  a.n_tensors = n_tensors;
+  a.owner = owner;
+  a.owner_base = owner_base;
+  a.dense = dense;
+  a.dense_total = dense_total;
+  if (to_dense) {
+    static const uint32_t per_cu = blocks_per_cu(dense_kernel<true>);
+    hipLaunchKernelGGL(dense_kernel<true>, persistent_grid(per_cu, n_chunks, cus, 0), kBlock, 0,
+                       stream, a);
+  } else {
+    static const uint32_t per_cu = blocks_per_cu(dense_kernel<false>);
+    hipLaunchKernelGGL(dense_kernel<false>, persistent_grid(per_cu, n_chunks, cus, 0), kBlock, 0,
+                       stream, a);
+  }
+  return launch_status(who);
+}
+}  // namespace
+
+extern "C" int zero_owner_to_dense(const zero_chunk* chunks, uint64_t n_chunks, uint64_t begin,
+                                   uint64_t end, const uint64_t* tensor_offset,
+                                   const uint64_t* dense_offset, uint32_t n_tensors,
+                                   const float* owner, uint64_t owner_base, float* dense,
+                                   uint64_t dense_total, hipStream_t stream) {
+  return dense_copy(true, chunks, n_chunks, begin, end, tensor_offset, dense_offset, n_tensors,
+                    const_cast<float*>(owner), owner_base, dense, dense_total, stream,
+                    "zero_owner_to_dense");
+}
+
+extern "C" int zero_dense_to_owner(const zero_chunk* chunks, uint64_t n_chunks, uint64_t begin,
+                                   uint64_t end, const uint64_t* tensor_offset,
+                                   const uint64_t* dense_offset, uint32_t n_tensors,
+                                   const float* dense, uint64_t dense_total, float* owner,
+                                   uint64_t owner_base, hipStream_t stream) {
+  return dense_copy(false, chunks, n_chunks, begin, end, tensor_offset, dense_offset, n_tensors,
+                    owner, owner_base, const_cast<float*>(dense), dense_total, stream,
+                    "zero_dense_to_owner");
+}
+
+extern "C" int zero_copy_spans(const zero_copy_span* spans, uint64_t n_spans, const void* const* srcs,
+                               const uint64_t* src_numel, uint32_t n_srcs, void* dst,
+                               uint64_t dst_numel, uint32_t elem_bytes, hipStream_t stream) {
+  static const char* who = "zero_copy_spans";
+  clear_error();
+  if (elem_bytes != 2 && elem_bytes != 4) return fail(ZERO_EINVAL, "%s: elem_bytes must be 2 or 4", who);
+  if (n_spans == 0) return ZERO_OK;
+  if (!spans || !dst) return fail(ZERO_EINVAL, "%s: NULL spans or dst", who);
+  if (n_srcs == 0 || n_srcs > ZERO_MAX_COPY_SOURCES)
+    return fail(ZERO_EINVAL, "%s: n_srcs = %u outside [1, %d]", who, n_srcs, ZERO_MAX_COPY_SOURCES);
+  if (!srcs || !src_numel) return fail(ZERO_EINVAL, "%s: NULL source arrays", who);
+  if (!aligned16(dst)) return fail(ZERO_EINVAL, "%s: dst is not 16-byte aligned", who);
+  SpanArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (uint32_t i = 0; i < n_srcs; ++i) {
+    if (!srcs[i]) return fail(ZERO_EINVAL, "%s: source %u is NULL", who, i);
+    if (!aligned16(srcs[i])) return fail(ZERO_EINVAL, "%s: source %u is not 16-byte aligned", who, i);
+    a.src[i] = srcs[i];
+    a.src_numel[i] = src_numel[i];
+  }
+  a.spans = spans;
+  a.n_spans = n_spans;
+  a.n_srcs = n_srcs;
+  a.dst = dst;
+  a.dst_numel = dst_numel;
+  int cus = 0;
+  int rc = cu_count(&cus);
+  if (rc) return rc;
+  if (elem_bytes == 2) {
+    static const uint32_t per_cu = blocks_per_cu(span_kernel<uint16_t>);
+    hipLaunchKernelGGL(span_kernel<uint16_t>, persistent_grid(per_cu, n_spans, cus, 0), kBlock, 0,
+                       stream, a);
+  } else {
+    static const uint32_t per_cu = blocks_per_cu(span_kernel<uint32_t>);
+    hipLaunchKernelGGL(span_kernel<uint32_t>, persistent_grid(per_cu, n_spans, cus, 0), kBlock, 0,
+                       stream, a);
+  }
+  return launch_status(who);
+}

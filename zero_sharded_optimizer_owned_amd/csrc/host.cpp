@@ -172,3 +172,124 @@ extern "C" int zero_clip_coef(double sumsq, double max_norm, double eps, float* 
   *coef = (float)(c < 1.0 ? c : 1.0);
   return ZERO_OK;
 }
+
+// ---------------------------------------------------------------------------
+// ZeRO-3 per-tensor partitioning ([Deep dive] "Stage 3 needs a live working
+// set"): tensor k is cut into R shards of s_k = ceil(n_k / R) elements; rank
+// r's shard buffer holds its shard of every tensor in tensor order (tensor k
+// at so_k = sum of s_j, j < k); a live tensor is gathered into a separate
+// full buffer of R * s_k elements, shards in rank order.
+// ---------------------------------------------------------------------------
+namespace {
+int check_stage3(const uint64_t* numel, uint32_t n_tensors, uint32_t ranks, const uint32_t* live,
+                 uint32_t n_live, const char* who) {
+  if (ranks == 0) return fail(ZERO_EINVAL, "%s: ranks must be >= 1", who);
+  if (n_tensors == 0 || !numel) return fail(ZERO_EINVAL, "%s: no tensors", who);
+  for (uint32_t k = 0; k < n_tensors; ++k)
+    if (numel[k] == 0) return fail(ZERO_EINVAL, "%s: tensor %u has 0 elements", who, k);
+  if (n_live > 0 && !live) return fail(ZERO_EINVAL, "%s: live is NULL", who);
+  for (uint32_t i = 0; i < n_live; ++i) {
+    if (live[i] >= n_tensors) return fail(ZERO_EINVAL, "%s: live tensor %u out of range", who, live[i]);
+    for (uint32_t j = 0; j < i; ++j)
+      if (live[j] == live[i]) return fail(ZERO_EINVAL, "%s: live tensor %u listed twice", who, live[i]);
+  }
+  return ZERO_OK;
+}
+
+uint64_t shard_of(uint64_t n, uint32_t ranks) { return n / ranks + (n % ranks != 0); }
+
+// Append [src, src+len) -> [dst, dst+len) of buffer `buf`, cut into pieces of at most C.
+void add_spans(uint64_t src, uint64_t dst, uint64_t len, uint32_t buf, uint64_t C, zero_copy_span* out,
+               uint64_t capacity, uint64_t* count) {
+  while (len > 0) {
+    const uint64_t piece = len < C ? len : C;
+    if (out && *count < capacity) {
+      out[*count].src = src;
+      out[*count].dst = dst;
+      out[*count].len = (uint32_t)piece;
+      out[*count].buf = buf;
+    }
+    ++*count;
+    src += piece;
+    dst += piece;
+    len -= piece;
+  }
+}
+
+int finish_spans(zero_copy_span* out, uint64_t capacity, uint64_t count, uint64_t* n_spans,
+                 const char* who) {
+  *n_spans = count;
+  if (out == nullptr && capacity == 0) return ZERO_OK;
+  if (count > capacity)
+    return fail(ZERO_ERANGE, "%s: %llu spans needed, capacity %llu", who, (unsigned long long)count,
+                (unsigned long long)capacity);
+  return ZERO_OK;
+}
+}  // namespace
+
+extern "C" int zero3_storage(const uint64_t* numel, uint32_t n_tensors, uint32_t ranks,
+                             const uint32_t* live, uint32_t n_live, uint64_t* shard_numel,
+                             uint64_t* resident, uint64_t* gathered) {
+  zs::clear_error();
+  static const char* who = "zero3_storage";
+  int rc = check_stage3(numel, n_tensors, ranks, live, n_live, who);
+  if (rc) return rc;
+  if (!resident || !gathered) return fail(ZERO_EINVAL, "%s: NULL output", who);
+  u128 res = 0, gat = 0;
+  for (uint32_t k = 0; k < n_tensors; ++k) res += shard_of(numel[k], ranks);
+  for (uint32_t i = 0; i < n_live; ++i) gat += (u128)shard_of(numel[live[i]], ranks) * ranks;
+  if (res > (u128)UINT64_MAX || gat > (u128)UINT64_MAX)
+    return fail(ZERO_ERANGE, "%s: counts exceed 64 bits", who);
+  if (shard_numel)
+    for (uint32_t k = 0; k < n_tensors; ++k) shard_numel[k] = shard_of(numel[k], ranks);
+  *resident = (uint64_t)res;
+  *gathered = (uint64_t)gat;
+  return ZERO_OK;
+}
+
+extern "C" int zero3_gather_spans(const uint64_t* numel, uint32_t n_tensors, uint32_t ranks,
+                                  const uint32_t* live, uint32_t n_live, uint32_t max_span,
+                                  zero_copy_span* out, uint64_t capacity, uint64_t* n_spans) {
+  zs::clear_error();
+  static const char* who = "zero3_gather_spans";
+  int rc = check_stage3(numel, n_tensors, ranks, live, n_live, who);
+  if (rc) return rc;
+  if (!n_spans) return fail(ZERO_EINVAL, "%s: n_spans is NULL", who);
+  if (max_span == 0) return fail(ZERO_EINVAL, "%s: max_span must be >= 1", who);
+  if (capacity > 0 && !out) return fail(ZERO_EINVAL, "%s: out is NULL", who);
+  uint64_t count = 0, gbase = 0;
+  for (uint32_t i = 0; i < n_live; ++i) {
+    const uint32_t k = live[i];
+    uint64_t so = 0;
+    for (uint32_t j = 0; j < k; ++j) so += shard_of(numel[j], ranks);
+    const uint64_t s = shard_of(numel[k], ranks);
+    for (uint32_t r = 0; r < ranks; ++r) add_spans(so, gbase + (uint64_t)r * s, s, r, max_span, out, capacity, &count);
+    gbase += (uint64_t)ranks * s;
+  }
+  return finish_spans(out, capacity, count, n_spans, who);
+}
+
+extern "C" int zero3_partition_spans(const uint64_t* numel, uint32_t n_tensors, uint32_t ranks,
+                                     uint32_t rank, uint32_t max_span, zero_copy_span* out,
+                                     uint64_t capacity, uint64_t* n_spans) {
+  zs::clear_error();
+  static const char* who = "zero3_partition_spans";
+  int rc = check_stage3(numel, n_tensors, ranks, nullptr, 0, who);
+  if (rc) return rc;
+  if (!n_spans) return fail(ZERO_EINVAL, "%s: n_spans is NULL", who);
+  if (rank >= ranks) return fail(ZERO_EINVAL, "%s: rank %u >= ranks %u", who, rank, ranks);
+  if (max_span == 0) return fail(ZERO_EINVAL, "%s: max_span must be >= 1", who);
+  if (capacity > 0 && !out) return fail(ZERO_EINVAL, "%s: out is NULL", who);
+  uint64_t count = 0, so = 0, dense = 0;
+  for (uint32_t k = 0; k < n_tensors; ++k) {
+    const uint64_t s = shard_of(numel[k], ranks);
+    const uint64_t first = (uint64_t)rank * s;
+    if (first < numel[k]) {
+      const uint64_t len = numel[k] - first < s ? numel[k] - first : s;
+      add_spans(dense + first, so, len, 0, max_span, out, capacity, &count);
+    }
+    so += s;
+    dense += numel[k];
+  }
+  return finish_spans(out, capacity, count, n_spans, who);
+}

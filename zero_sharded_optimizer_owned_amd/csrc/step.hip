@@ -1,5 +1,6 @@
-// Device half of libzero_shard: HIP kernels for gfx950 and the C entry points
-// that validate, plan and launch them.
+// The hot path of libzero_shard: rank reduce, overflow/norm check and the
+// fused Adam/AdamW step -- HIP kernels for gfx950 and the C entry points that
+// validate, plan and launch them.
 //
 // All kernels stream HBM: the step moves ~34-162 bytes per owned parameter for
 // a few dozen fp32 operations, so the design aims at bytes in flight, not at
@@ -27,12 +28,11 @@
 #include <cstring>
 
 #include "internal.h"
+#include "launch.h"
 
 namespace zs {
 namespace {
 
-constexpr int kBlock = 256;
-constexpr int kWavesPerBlock = kBlock / 64;
 constexpr int kMaxPartials = 4096;  // per-block partials the check workspace holds
 // Flat-range kernels hand out work in tiles: one wavefront streams a contiguous
 // span of every stream (up to 512 vectors = 4096 elements) before taking the
@@ -559,82 +559,8 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Export / import between an owner's shard and the dense per-tensor layout.
-// ---------------------------------------------------------------------------
-struct DenseArgs {
-  const zero_chunk* chunks;
-  uint64_t n_chunks;
-  uint64_t begin, end;
-  const uint64_t* tensor_offset;  // [n_tensors] flat start of each tensor
-  const uint64_t* dense_offset;   // [n_tensors] dense start of each tensor
-  uint32_t n_tensors;
-  float* owner;                   // element f - owner_base
-  uint64_t owner_base;
-  float* dense;                   // [dense_total]
-  uint64_t dense_total;
-};
-
-// Each wavefront copies whole chunks, 64 consecutive elements per instruction
-// on both sides, four instructions in flight per lane.  Chunks whose tensor
-// index or position disagrees with the tables are skipped, and no dense
-// index at or past dense_total is touched.
-template <bool TO_DENSE>
-__global__ void __launch_bounds__(kBlock) dense_kernel(const DenseArgs a) {
-  const uint64_t lane = threadIdx.x & 63;
-  const uint64_t wave =
-      __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-  const uint64_t n_waves = (uint64_t)gridDim.x * kWavesPerBlock;
-  for (uint64_t c = wave; c < a.n_chunks; c += n_waves) {
-    const zero_chunk ch = a.chunks[c];
-    if (ch.tensor >= a.n_tensors) continue;
-    const uint64_t toff = a.tensor_offset[ch.tensor];
-    const uint64_t doff = a.dense_offset[ch.tensor];
-    const uint64_t f0 = max(max(ch.flat, a.begin), toff);
-    const uint64_t f1 = min(ch.flat + ch.len, a.end);
-    for (uint64_t f = f0 + lane; f < f1; f += 256) {
-      float x[4];
-      uint64_t d[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint64_t fj = f + 64 * j;
-        d[j] = fj < f1 ? doff + (fj - toff) : a.dense_total;
-        if (d[j] < a.dense_total) x[j] = TO_DENSE ? a.owner[fj - a.owner_base] : a.dense[d[j]];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (d[j] < a.dense_total) {
-          if (TO_DENSE) a.dense[d[j]] = x[j];
-          else a.owner[f + 64 * j - a.owner_base] = x[j];
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Host-side planning and validation.
 // ---------------------------------------------------------------------------
-constexpr int kMaxDevices = 64;
-int g_cu_count[kMaxDevices];  // 0 = not yet queried
-
-int cu_count(int* out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(ZERO_EHIP, "hipGetDevice failed");
-  if (dev >= 0 && dev < kMaxDevices && __atomic_load_n(&g_cu_count[dev], __ATOMIC_RELAXED) > 0) {
-    *out = __atomic_load_n(&g_cu_count[dev], __ATOMIC_RELAXED);
-    return ZERO_OK;
-  }
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    return fail(ZERO_EHIP, "querying the compute-unit count failed");
-  if (dev >= 0 && dev < kMaxDevices) __atomic_store_n(&g_cu_count[dev], cus, __ATOMIC_RELAXED);
-  *out = cus;
-  return ZERO_OK;
-}
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
 bool is_pow2_float(float d, float* inv) {
   int e = 0;
   const float mant = std::frexp(d, &e);
@@ -711,12 +637,6 @@ FlatPlan flat_plan(uint64_t n_vectors, int cus, uint32_t cap) {
   return FlatPlan{want == 0 ? 1u : (uint32_t)want, tile};
 }
 
-int launch_status(const char* who) {
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(ZERO_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
-  return ZERO_OK;
-}
-
 template <int DT, int MODE>
 void launch_reduce_m(const ReduceArgs& a, bool check, uint32_t grid, hipStream_t s) {
   if (check) hipLaunchKernelGGL((reduce_kernel<DT, MODE, true>), grid, kBlock, 0, s, a);
@@ -728,23 +648,6 @@ void launch_reduce(const ReduceArgs& a, int mode, bool check, uint32_t grid, hip
   if (mode == kStartFromOut) launch_reduce_m<DT, kStartFromOut>(a, check, grid, s);
   else if (mode == kAddMean) launch_reduce_m<DT, kAddMean>(a, check, grid, s);
   else launch_reduce_m<DT, kOverwrite>(a, check, grid, s);
-}
-
-// Blocks of `kernel` that fit on one CU at once.
-template <typename K>
-uint32_t blocks_per_cu(K kernel) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kBlock, 0) != hipSuccess || n < 1) n = 1;
-  return (uint32_t)n;
-}
-
-// A persistent grid: every block resident at once, but no more blocks than
-// there are chunks for their wavefronts.
-uint32_t persistent_grid(uint32_t per_cu, uint64_t n_chunks, int cus, uint32_t requested) {
-  if (requested) return requested;
-  const uint64_t resident = (uint64_t)per_cu * (uint64_t)cus;
-  const uint64_t by_chunks = (n_chunks + kWavesPerBlock - 1) / kWavesPerBlock;
-  return (uint32_t)(by_chunks < resident ? by_chunks : resident);
 }
 
 template <int GDT, int PDT, int RC>
@@ -930,64 +833,3 @@ extern "C" int zero_adam_step(const zero_adam_args* p, hipStream_t stream) {
   return launch_status(who);
 }
 
-namespace {
-int dense_copy(bool to_dense, const zero_chunk* chunks, uint64_t n_chunks, uint64_t begin,
-               uint64_t end, const uint64_t* tensor_offset, const uint64_t* dense_offset,
-               uint32_t n_tensors, float* owner, uint64_t owner_base, float* dense,
-               uint64_t dense_total, hipStream_t stream, const char* who) {
-  clear_error();
-  if (begin > end) return fail(ZERO_EINVAL, "%s: begin > end", who);
-  if (n_chunks > 0 && (!chunks || !tensor_offset || !dense_offset || !owner || !dense))
-    return fail(ZERO_EINVAL, "%s: NULL pointer argument", who);
-  if (n_tensors == 0 && n_chunks > 0) return fail(ZERO_EINVAL, "%s: no tensors", who);
-  if (owner_base > begin) return fail(ZERO_EINVAL, "%s: owner_base lies above begin", who);
-  if ((reinterpret_cast<uintptr_t>(owner) | reinterpret_cast<uintptr_t>(dense)) & 3u)
-    return fail(ZERO_EINVAL, "%s: fp32 buffers must be 4-byte aligned", who);
-  if (n_chunks == 0 || begin == end) return ZERO_OK;
-  int cus = 0;
-  int rc = cu_count(&cus);
-  if (rc) return rc;
-  DenseArgs a;
-  a.chunks = chunks;
-  a.n_chunks = n_chunks;
-  a.begin = begin;
-  a.end = end;
-  a.tensor_offset = tensor_offset;
-  a.dense_offset = dense_offset;
-  a.n_tensors = n_tensors;
-  a.owner = owner;
-  a.owner_base = owner_base;
-  a.dense = dense;
-  a.dense_total = dense_total;
-  if (to_dense) {
-    static const uint32_t per_cu = blocks_per_cu(dense_kernel<true>);
-    hipLaunchKernelGGL(dense_kernel<true>, persistent_grid(per_cu, n_chunks, cus, 0), kBlock, 0,
-                       stream, a);
-  } else {
-    static const uint32_t per_cu = blocks_per_cu(dense_kernel<false>);
-    hipLaunchKernelGGL(dense_kernel<false>, persistent_grid(per_cu, n_chunks, cus, 0), kBlock, 0,
-                       stream, a);
-  }
-  return launch_status(who);
-}
-}  // namespace
-
-extern "C" int zero_owner_to_dense(const zero_chunk* chunks, uint64_t n_chunks, uint64_t begin,
-                                   uint64_t end, const uint64_t* tensor_offset,
-                                   const uint64_t* dense_offset, uint32_t n_tensors,
-                                   const float* owner, uint64_t owner_base, float* dense,
-                                   uint64_t dense_total, hipStream_t stream) {
-  return dense_copy(true, chunks, n_chunks, begin, end, tensor_offset, dense_offset, n_tensors,
-                    const_cast<float*>(owner), owner_base, dense, dense_total, stream,
-                    "zero_owner_to_dense");
-}
-
-extern "C" int zero_dense_to_owner(const zero_chunk* chunks, uint64_t n_chunks, uint64_t begin,
-                                   uint64_t end, const uint64_t* tensor_offset,
-                                   const uint64_t* dense_offset, uint32_t n_tensors,
-                                   const float* dense, uint64_t dense_total, float* owner,
-                                   uint64_t owner_base, hipStream_t stream) {
-  return dense_copy(false, chunks, n_chunks, begin, end, tensor_offset, dense_offset, n_tensors,
-                    owner, owner_base, const_cast<float*>(dense), dense_total, stream,
-                    "zero_dense_to_owner");
-}
