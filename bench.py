@@ -34,6 +34,7 @@ METRIC = "owned-shard params updated/sec + achieved HBM GB/s (fraction of MI355X
 PEAK_GBPS = 8000.0
 HP = dict(lr=1e-3, beta1=0.8, beta2=0.999, eps=1e-8, weight_decay=3e-7, adamw=True)
 FIRST_STEP = 11  # the state stands for an optimizer after ten warm-up updates
+DEFAULT_CHUNK = 2048  # chunk-table granularity (elements) of the timed launches
 
 
 def parse():
@@ -46,7 +47,7 @@ def parse():
                     help="config 5 only: accumulate microsteps locally then reduce (default), or reduce "
                          "every microstep and add the owned mean to an fp32 accumulator")
     ap.add_argument("--grid", type=int, default=0, help="persistent grid blocks (0: library default)")
-    ap.add_argument("--chunk", type=int, default=4096, help="max chunk elements")
+    ap.add_argument("--chunk", type=int, default=DEFAULT_CHUNK, help="max chunk elements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--op", default="step", choices=("step", "export", "gather3"),
@@ -66,6 +67,10 @@ def kernel_source_hash() -> str:
     for name in STEP_SOURCES:
         h.update(open(os.path.join(CSRC, name), "rb").read())
     return h.hexdigest()[:16]
+
+
+# Workload names used in profiles/ file names.
+WORKLOAD_TAG = {2: "flat-1.5e9-R4", 3: "llama-6.6e9-R8", 4: "flat-7e10-R64", 5: "10k-tensors-2e9-R16"}
 
 
 def traffic_record(name: str):
@@ -231,10 +236,14 @@ class Workload:
         self.grads = [None]
 
     def algorithmic_bytes(self) -> int:
-        """Bytes the dominant kernel must move per launch."""
+        """Bytes the dominant kernel (the one that takes most of the step) moves per launch."""
         n = self.sh.n_real
         if self.cfg == 4:
-            return n * 30  # adam from the stored gradient: g 4 + w,m,v 12 + 12 + p16 2
+            # the 64-rank reduce with the fused check: 64 fp16 reads + one fp32 write
+            return (self.sh.end - self.sh.begin) * (self.R * 2 + 4)
+        if self.cfg == 5 and self.schedule == "accumulate":
+            # one later microstep of the local accumulation: bf16 read, fp32 read and write
+            return self.sh.padded_total * 10
         if self.schedule == "per-backward":
             # one microstep's reduce of 16 bf16 slices into the accumulator: 16*2 + 4 + 4
             return (self.sh.end - self.sh.begin) * (self.R * 2 + 8)
@@ -250,7 +259,7 @@ class Workload:
             return span * (self.R * 2 + 4) + 7 * span * (self.R * 2 + 8) + n * 30
         if self.cfg == 5:
             P = self.sh.padded_total
-            return P * (6 + 7 * 10) + self.kernel_bytes
+            return P * (6 + 7 * 10) + n * (self.R * 4 + 26)
         return self.kernel_bytes
 
     # one full step of the owner's hot path
@@ -275,7 +284,16 @@ class Workload:
             return False
         if self.cfg == 5:
             for k, g in enumerate(self.micro):
+                if timing is not None and k == 7:
+                    timing[0].record()
                 zs.zero_reduce_owned([g], 0, sh.padded_total, 1.0, self.acc, accumulate=k > 0)
+                if timing is not None and k == 7:
+                    timing[1].record()
+            sh.adam_step(step=self.t, hyper=HP, rank_grads=self.grads, grad_base=sh.local_base,
+                         divisor=self.divisor, param16=self.p16, param_base=self.param_base,
+                         grid_blocks=self.grid)
+            self.t += 1
+            return False
         self.calls += 1
         if self.cfg == 4:
             inject = self.calls % 4 == 0  # one step in four carries an inf and a NaN
@@ -283,9 +301,13 @@ class Workload:
                 saved = (self.grads[5][12345].clone(), self.grads[17][777_777].clone())
                 self.grads[5][12345] = float("inf")
                 self.grads[17][777_777] = float("nan")
+            if timing is not None:
+                timing[0].record()
             zs.zero_reduce_owned(self.grads, sh.begin, sh.end - sh.begin, self.divisor, self.g32,
                                  grad_base=sh.local_base, out_base=sh.local_base,
                                  check=(self.ov, self.ss, self.ws))
+            if timing is not None:
+                timing[1].record()
             flag, sumsq = int(self.ov.item()), float(self.ss.item())  # 12 bytes to the host
             if inject:
                 self.grads[5][12345] = saved[0]
@@ -294,12 +316,8 @@ class Workload:
                 self.skipped += 1
                 return True
             coef = zs.zero_clip_coef(sumsq, 1.0, 1e-6)
-            if timing is not None:
-                timing[0].record()
             sh.adam_step(step=self.t, hyper=HP, reduced_g=self.g32, param16=self.p16,
                          param_base=self.param_base, clip_coef=coef, grid_blocks=self.grid)
-            if timing is not None:
-                timing[1].record()
             self.t += 1
             return False
         if timing is not None:
@@ -430,7 +448,7 @@ class Stage3Gather:
             fill(t, self.SEED, synth.STREAM_MASTER, r, 0, synth.DIST_NORMAL, 0.02)
             self.shards.append(t)
         self.out = torch.empty(self.gathered, dtype=torch.bfloat16, device="cuda")
-        self.spans = zs.zero3_gather_spans(self.numels, R, self.live, max_span=1 << 16)
+        self.spans = zs.zero3_gather_spans(self.numels, R, self.live)
         self.spans_dev = zs.spans_to_device(self.spans)
         self.so = np.concatenate([[0], np.cumsum(self.shard_numel)[:-1]]).astype(np.int64)
         torch.cuda.synchronize()
@@ -615,7 +633,7 @@ def main():
     wall = time.perf_counter() - wall0
     total_ms = t_all0.elapsed_time(t_all1)
     ms_step = total_ms / args.steps
-    kms = [s.elapsed_time(e) for s, e, ok in zip(starts, ends, launched) if ok]
+    kms = [s.elapsed_time(e) for s, e in zip(starts, ends)]  # the dominant kernel runs every step
     kernel_ms = sum(kms) / len(kms)
     n = w.sh.n_real
     updated = n * (args.steps - overflow_steps)
@@ -623,11 +641,13 @@ def main():
     step_bytes = sum(w.step_bytes(not ok) for ok in launched)
     gbps_step = step_bytes / (total_ms / 1e3) / 1e9
     achieved = w.kernel_bytes / (kernel_ms / 1e3) / 1e9
-    kname = "adam_step_" + {2: "f16_f16", 3: "bf16_bf16", 4: "reduced_f16", 5: "f32_bf16"}[args.config]
+    kname = {2: "adam_step_f16_f16", 3: "adam_step_bf16_bf16", 4: "reduce_check_f16_r64",
+             5: "accumulate_bf16"}[args.config]
     if w.schedule == "per-backward":
         kname = "reduce_add_mean_bf16_r16"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic_record(f"{kname}_config{args.config}"),
+                "frac": round(achieved / PEAK_GBPS, 4),
+                "traffic": traffic_record(f"{kname}__{WORKLOAD_TAG[args.config]}"),
                 "kernel": kname, "kernel_ms": round(kernel_ms, 4),
                 "bytes_per_launch": w.kernel_bytes}
     line = {

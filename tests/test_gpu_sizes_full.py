@@ -154,7 +154,7 @@ def _check_coverage(w):
 
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_fused_step_full_size(cfg):
-    w = bench.Workload(cfg, 4096, 0)
+    w = bench.Workload(cfg, bench.DEFAULT_CHUNK, 0)
     idx = _sample(w)
     print(f"config {cfg}: {w.sh.n_real} owned, {w.sh.chunks.size} chunks, {idx.size} sampled", flush=True)
     w.step()
@@ -167,7 +167,7 @@ def test_fused_step_full_size(cfg):
 
 def test_loss_scaled_two_pass_full_size():
     """70e9 / R=64 owner: fused reduce + check, then AdamW from the stored gradient."""
-    w = bench.Workload(4, 4096, 0)
+    w = bench.Workload(4, bench.DEFAULT_CHUNK, 0)
     sh = w.sh
     idx = _sample(w, n_random=10_000)
     print(f"config 4: {sh.n_real} owned, {idx.size} sampled", flush=True)
@@ -206,7 +206,7 @@ def test_loss_scaled_two_pass_full_size():
 
 def test_accumulation_and_owner_step_full_size():
     """10,000 tensors, R=16: eight bf16 microsteps into fp32, then the fused owner step."""
-    w = bench.Workload(5, 4096, 0)
+    w = bench.Workload(5, bench.DEFAULT_CHUNK, 0)
     sh = w.sh
     idx = _sample(w, n_random=5_000)
     print(f"config 5: {sh.n_real} owned, {sh.chunks.size} chunks, {idx.size} sampled", flush=True)
@@ -232,7 +232,7 @@ def test_accumulation_and_owner_step_full_size():
 def test_per_backward_schedule_full_size():
     """Config 5 sizes under the per-backward schedule: every microstep reduces the 16 ranks'
     owned bf16 slices and adds the mean to the owner's fp32 accumulator; AdamW at the end."""
-    w = bench.Workload(5, 4096, 0, "per-backward")
+    w = bench.Workload(5, bench.DEFAULT_CHUNK, 0, "per-backward")
     sh = w.sh
     idx = _sample(w, n_random=5_000)
     print(f"config 5 per-backward: {sh.n_real} owned, {idx.size} sampled", flush=True)

@@ -361,12 +361,12 @@ def _spans(fn, *args, max_span):
     return out
 
 
-def zero3_gather_spans(numels, ranks: int, live, max_span: int = 1 << 16) -> np.ndarray:
+def zero3_gather_spans(numels, ranks: int, live, max_span: int = 2048) -> np.ndarray:
     n, lv = _u64(numels), _live(live)
     return _spans(lib().zero3_gather_spans, _p(n), n.size, ranks, _p(lv), lv.size, max_span=max_span)
 
 
-def zero3_partition_spans(numels, ranks: int, rank: int, max_span: int = 1 << 16) -> np.ndarray:
+def zero3_partition_spans(numels, ranks: int, rank: int, max_span: int = 2048) -> np.ndarray:
     n = _u64(numels)
     return _spans(lib().zero3_partition_spans, _p(n), n.size, ranks, rank, max_span=max_span)
 
@@ -409,7 +409,7 @@ class OwnerShard:
     """
 
     def __init__(self, numels: Sequence[int], ranks: int, owner: int, align: int = 64,
-                 max_chunk: int = 4096, device=None):
+                 max_chunk: int = 2048, device=None):
         torch = _torch()
         self.numels = [int(x) for x in numels]
         self.offsets, self.padded_total, begins, ends = zero_shard_layout(self.numels, ranks, align)
