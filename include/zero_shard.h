@@ -25,8 +25,9 @@
  *     gives a message (thread-local, valid until the next call on the thread).
  *     No exceptions escape, nothing exits the process.
  *   - The caller owns every buffer.  The library allocates no memory and
- *     keeps no state between calls (apart from a per-device cache of the
- *     compute-unit count).  Arguments are validated before anything is
+ *     keeps no state between calls apart from two read-only caches: the
+ *     compute-unit count of each device and the occupancy of each kernel
+ *     (filled on first use).  Arguments are validated before anything is
  *     launched; a call that fails validation launches nothing and writes
  *     nothing.  Buffer extents cannot be seen through plain pointers: the
  *     caller guarantees the sizes stated for each argument.

@@ -319,7 +319,7 @@ def _tiny_run(owners, grads_fn, steps=5):
             ch = zs.zero_chunk_table([P], [0], b, e, 8)
             zs.zero_adam_step(chunks_dev=zs.chunks_to_device(ch), n_chunks=ch.size, begin=b, end=e,
                               master=w[lb:], exp_avg=m[lb:], exp_avg_sq=v[lb:], local_base=lb,
-                              step=t, rank_grads=rows, divisor=float(R), max_flat=e, **hp)
+                              step=t, rank_grads=rows, divisor=float(R), **hp)
     return from_dev(w)[:P], from_dev(m)[:P], from_dev(v)[:P]
 
 
@@ -405,3 +405,42 @@ def test_per_backward_schedule_matches_oracle():
     assert_state_close(from_dev(dm), m, "m")
     assert_state_close(from_dev(dv), v, "v")
     assert_p16_within_ulp(from_dev(dp), p_or, "p16")
+
+
+# ---------------------------------------------------------------- launch-shape independence
+def _fused_once(numels, R, A, owner, max_chunk, grid_blocks, chunks_override=None):
+    off, total, begin, end, lb, grads, w, m, v = _owner_inputs(numels, R, A, owner, F16, 77)
+    chunks = chunks_override if chunks_override is not None else zs.zero_chunk_table(numels, off, begin, end, max_chunk)
+    dw, dm, dv = to_dev(w, F32), to_dev(m, F32), to_dev(v, F32)
+    dp = torch.zeros(total + 8, dtype=torch.float16, device=DEV)
+    zs.zero_adam_step(chunks_dev=zs.chunks_to_device(chunks), n_chunks=chunks.size, begin=begin, end=end,
+                      master=dw, exp_avg=dm, exp_avg_sq=dv, local_base=lb, step=4,
+                      rank_grads=[to_dev(g, F16) for g in grads], divisor=float(R), param16=dp,
+                      grid_blocks=grid_blocks, **HP)
+    return [from_dev(x) for x in (dw, dm, dv, dp)]
+
+
+def test_fused_step_is_deterministic_and_independent_of_grid_and_chunking():
+    numels, R, A, owner = [10_000, 37, 70_001, 5], 4, 64, 1
+    ref = _fused_once(numels, R, A, owner, 2048, 0)
+    again = _fused_once(numels, R, A, owner, 2048, 0)
+    for a, b in zip(ref, again):
+        assert_bits_equal(a, b, "run to run")
+    for chunk, grid in ((8, 0), (64, 1), (2048, 1), (2048, 3), (16384, 7), (1 << 20, 0)):
+        got = _fused_once(numels, R, A, owner, chunk, grid)
+        for a, b in zip(ref, got):
+            assert_bits_equal(a, b, f"chunk {chunk} grid {grid}")
+
+
+def test_chunks_outside_the_owner_range_are_ignored():
+    numels, R, A, owner = [5000, 3000], 3, 8, 1
+    off, total, b, e = zs.zero_shard_layout(numels, R, A)
+    begin, end = int(b[owner]), int(e[owner])
+    good = zs.zero_chunk_table(numels, off, begin, end, 512)
+    ref = _fused_once(numels, R, A, owner, 512, 0)
+    # a table that also names elements of the neighbouring owners: clamped to [begin, end)
+    wide = zs.zero_chunk_table(numels, off, 0, total, 512)
+    got = _fused_once(numels, R, A, owner, 512, 0, chunks_override=wide)
+    for a, b_ in zip(ref, got):
+        assert_bits_equal(a, b_, "wide chunk table")
+    assert good.size < wide.size

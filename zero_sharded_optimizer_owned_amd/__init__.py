@@ -259,14 +259,14 @@ def zero_adam_step(*, chunks_dev, n_chunks: int, begin: int, end: int, master, e
                    local_base: int, step: int, lr: float, beta1: float, beta2: float, eps: float,
                    weight_decay: float = 0.0, adamw: bool = True, rank_grads=None, grad_base: int = 0,
                    divisor: float = 1.0, reduced_g=None, param16=None, param_base: int = 0,
-                   clip_coef: float = 1.0, grid_blocks: int = 0, max_flat: Optional[int] = None) -> None:
+                   clip_coef: float = 1.0, grid_blocks: int = 0) -> None:
     """Fused reduce + Adam/AdamW + 16-bit write-back over a device chunk table.
 
-    ``max_flat`` (default ``end``) bounds the flat indices the chunk table may
-    name; every buffer is checked to hold them.
+    The kernel touches only flat indices in [begin, end) (chunk pieces outside are
+    ignored), so every buffer is checked to hold those.
     """
     torch = _torch()
-    last = end if max_flat is None else max_flat
+    last = end
     if chunks_dev is not None:
         _dev(chunks_dev, "chunks")
         if chunks_dev.numel() * chunks_dev.element_size() < n_chunks * CHUNK_DTYPE.itemsize:

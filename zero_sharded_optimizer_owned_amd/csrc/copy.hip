@@ -150,7 +150,7 @@ int dense_copy(bool to_dense, const zero_chunk* chunks, uint64_t n_chunks, uint6
     return fail(ZERO_EINVAL, "%s: fp32 buffers must be 4-byte aligned", who);
   if (n_chunks == 0 || begin == end) return ZERO_OK;
   int cus = 0;
-  int rc = cu_count(&cus);
+  int rc = begin_launch(&cus);
   if (rc) return rc;
   DenseArgs a;
   a.chunks = chunks;
@@ -223,7 +223,7 @@ extern "C" int zero_copy_spans(const zero_copy_span* spans, uint64_t n_spans, co
   a.dst = dst;
   a.dst_numel = dst_numel;
   int cus = 0;
-  int rc = cu_count(&cus);
+  int rc = begin_launch(&cus);
   if (rc) return rc;
   if (elem_bytes == 2) {
     static const uint32_t per_cu = blocks_per_cu(span_kernel<uint16_t>);

@@ -14,6 +14,10 @@ constexpr int kWavesPerBlock = kBlock / 64;
 
 // Compute units of the current device (queried once per device).
 int cu_count(int* out);
+// Before an entry point's launches: clears a pending error left by earlier,
+// unrelated HIP calls (so launch_status reports only this call's launches)
+// and returns the compute-unit count.
+int begin_launch(int* cus);
 bool aligned16(const void* p);
 // ZERO_OK, or ZERO_EHIP with a message if the last launch failed.
 int launch_status(const char* who);

@@ -725,7 +725,7 @@ extern "C" int zero_reduce_owned(const void* const* rank_grads, uint32_t R, int 
   }
   if (n == 0) return ZERO_OK;
   int cus = 0;
-  if ((rc = cu_count(&cus))) return rc;
+  if ((rc = begin_launch(&cus))) return rc;
   a.begin = begin;
   a.end = begin + n;
   a.out = out;
@@ -757,7 +757,7 @@ extern "C" int zero_grad_check(const float* g, uint64_t n, int32_t* d_overflow, 
   if (n > 0 && !g) return fail(ZERO_EINVAL, "%s: g is NULL", who);
   if (n > 0 && !aligned16(g)) return fail(ZERO_EINVAL, "%s: g is not 16-byte aligned", who);
   int cus = 0;
-  if ((rc = cu_count(&cus))) return rc;
+  if ((rc = begin_launch(&cus))) return rc;
   const FlatPlan plan = flat_plan(n / 8, cus, kMaxPartials);
   const uint32_t grid = plan.grid;
   const CheckOut chk = check_layout(workspace);
@@ -809,7 +809,7 @@ extern "C" int zero_adam_step(const zero_adam_args* p, hipStream_t stream) {
     return fail(ZERO_EINVAL, "%s: betas must lie in [0, 1)", who);
   if (p->n_chunks == 0 || p->begin == p->end) return ZERO_OK;
   int cus = 0;
-  if ((rc = cu_count(&cus))) return rc;
+  if ((rc = begin_launch(&cus))) return rc;
 
   // Constants in fp64, each rounded once to fp32.
   const double t = (double)p->step;
