@@ -54,6 +54,8 @@ def parse():
                     help="step: the owner's optimizer step; export: copy the owner's fp32 master "
                          "into the dense per-tensor layout (checkpoint consolidation); gather3: the "
                          "ZeRO-3 gather of four Llama-style layers from 8 ranks' bf16 shard buffers")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-probe ceilings measured before the workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB fp32 device copy (counter calibration)")
     return ap.parse_args()
@@ -85,6 +87,61 @@ def traffic_record(name: str):
 
 
 # ---------------------------------------------------------------- workloads
+# read:write streams of equal size whose byte mix matches each dominant kernel's
+# algorithmic traffic per parameter (e.g. config 2: 20 B read, 14 B written)
+PROBE_MIX = {"adam_step_f16_f16": (10, 7), "adam_step_bf16_bf16": (2, 1), "reduce_check_f16_r64": (33, 1),
+             "accumulate_bf16": (3, 2), "reduce_add_mean_bf16_r16": (9, 1), "owner_to_dense": (1, 1),
+             "span_kernel<uint16_t>": (1, 1)}
+
+
+def probe_gbps(n_src: int, n_dst: int, total_bytes: float = 8e9, launches: int = 5) -> float:
+    """HBM GB/s of the library's streaming probe for an n_src:n_dst mix of
+    equal streams, about `total_bytes` moved per launch (far above the caches)."""
+    import torch
+
+    import zero_sharded_optimizer_owned_amd as zs
+
+    per = int(total_bytes // (n_src + n_dst)) // (1 << 20) * (1 << 20)
+    srcs = [torch.zeros(per, dtype=torch.uint8, device="cuda") for _ in range(n_src)]
+    dsts = [torch.empty(per, dtype=torch.uint8, device="cuda") for _ in range(n_dst)]
+    for _ in range(2):
+        zs.zero_stream_probe(srcs, dsts)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(launches):
+        zs.zero_stream_probe(srcs, dsts)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / launches
+    del srcs, dsts
+    torch.cuda.empty_cache()
+    return (n_src + n_dst) * per / (ms / 1e3) / 1e9
+
+
+def step_stats(ms: list) -> dict | None:
+    if not ms:
+        return None
+    v = sorted(ms)
+    mid = len(v) // 2
+    med = v[mid] if len(v) % 2 else 0.5 * (v[mid - 1] + v[mid])
+    return {"n": len(v), "median": round(med, 4), "min": round(v[0], 4), "max": round(v[-1], 4),
+            "mean": round(sum(v) / len(v), 4)}
+
+
+def ceilings(kname: str) -> dict:
+    """Measured ceilings for the dominant kernel: a plain copy and the probe
+    with the kernel's own read:write mix."""
+    n_src, n_dst = PROBE_MIX[kname]
+    return {"copy_gbps": round(probe_gbps(1, 1), 1), "mix": f"{n_src}:{n_dst}",
+            "mix_gbps": round(probe_gbps(n_src, n_dst), 1), "kernel": "zero_stream_probe"}
+
+
+def with_ceiling(roofline: dict, ceil: dict) -> dict:
+    a = roofline["achieved"]
+    return dict(ceil, frac_of_copy=round(a / ceil["copy_gbps"], 4), frac_of_mix=round(a / ceil["mix_gbps"], 4))
+
+
 def llama_numels():
     d, ff, vocab = 4096, 11008, 32000
     layer = [d * d] * 4 + [d * ff, d * ff, ff * d, d, d]
@@ -166,7 +223,7 @@ class Workload:
             self.g32 = torch.empty(end - lb, dtype=torch.float32, device=dev)
             self.ov = torch.zeros(1, dtype=torch.int32, device=dev)
             self.ss = torch.zeros(1, dtype=torch.float64, device=dev)
-            self.ws = zs.check_workspace(dev)
+            self.ws = zs.check_workspace(end - sh.begin, dev)
             self.divisor = float(R) * 65536.0
         else:
             self.p16 = torch.zeros(sh.padded_total, dtype=pdt, device=dev)
@@ -483,7 +540,7 @@ class Stage3Gather:
         return want
 
 
-def gather3_bench(args):
+def gather3_bench(args, ceil):
     import torch
 
     g = Stage3Gather()
@@ -510,6 +567,8 @@ def gather3_bench(args):
                      "unit": "GB/s", "frac": round(nbytes / (ms / 1e3) / 1e9 / PEAK_GBPS, 4), "traffic": None,
                      "kernel": "span_kernel<uint16_t>", "kernel_ms": round(ms, 4), "bytes_per_launch": nbytes},
     }
+    if ceil:
+        line["ceiling"] = with_ceiling(line["roofline"], ceil)
     if not args.no_cpu_baseline:
         import numpy as np
 
@@ -531,7 +590,7 @@ def gather3_bench(args):
     print(json.dumps(line), flush=True)
 
 
-def export_bench(w: Workload, args):
+def export_bench(w: Workload, args, ceil):
     """Time the consolidation copy of the owner's fp32 master into dense per-tensor weights."""
     import numpy as np
     import torch
@@ -563,6 +622,8 @@ def export_bench(w: Workload, args):
                      "unit": "GB/s", "frac": round(nbytes / (ms / 1e3) / 1e9 / PEAK_GBPS, 4), "traffic": None,
                      "kernel": "owner_to_dense", "kernel_ms": round(ms, 4), "bytes_per_launch": nbytes},
     }
+    if ceil:
+        line["ceiling"] = with_ceiling(line["roofline"], ceil)
     if not args.no_cpu_baseline:
         # the oracle's plain loop over the owner's first 2^16 real elements
         import synth
@@ -599,7 +660,17 @@ def main():
         sys.exit(1)
     zs.lib()
     if args.op == "gather3":
-        return gather3_bench(args)
+        kname = "span_kernel<uint16_t>"
+    elif args.op == "export":
+        kname = "owner_to_dense"
+    elif args.schedule == "per-backward":
+        kname = "reduce_add_mean_bf16_r16"
+    else:
+        kname = {2: "adam_step_f16_f16", 3: "adam_step_bf16_bf16", 4: "reduce_check_f16_r64",
+                 5: "accumulate_bf16"}[args.config]
+    ceil = None if args.no_ceiling else ceilings(kname)  # before the workload takes its memory
+    if args.op == "gather3":
+        return gather3_bench(args, ceil)
     if args.calibrate_copy:
         # a plain copy of known size: 2^28 fp32 read + 2^28 fp32 written per launch
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -610,7 +681,7 @@ def main():
         del src, dst
     w = Workload(args.config, args.chunk, args.grid, args.schedule)
     if args.op == "export":
-        return export_bench(w, args)
+        return export_bench(w, args, ceil)
     for _ in range(args.warmup):
         w.step()
     torch.cuda.synchronize()
@@ -619,19 +690,19 @@ def main():
     overflow_steps = 0
     w.skipped = 0
     torch.cuda.synchronize()
-    t_all0 = torch.cuda.Event(enable_timing=True)
-    t_all1 = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]  # step boundaries
     wall0 = time.perf_counter()
-    t_all0.record()
+    marks[0].record()
     launched = []
     for i in range(args.steps):
         skipped = w.step(timing=(starts[i], ends[i]))
+        marks[i + 1].record()
         launched.append(not skipped)
         overflow_steps += int(skipped)
-    t_all1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = t_all0.elapsed_time(t_all1)
+    total_ms = marks[0].elapsed_time(marks[-1])
+    step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
     ms_step = total_ms / args.steps
     kms = [s.elapsed_time(e) for s, e in zip(starts, ends)]  # the dominant kernel runs every step
     kernel_ms = sum(kms) / len(kms)
@@ -641,10 +712,6 @@ def main():
     step_bytes = sum(w.step_bytes(not ok) for ok in launched)
     gbps_step = step_bytes / (total_ms / 1e3) / 1e9
     achieved = w.kernel_bytes / (kernel_ms / 1e3) / 1e9
-    kname = {2: "adam_step_f16_f16", 3: "adam_step_bf16_bf16", 4: "reduce_check_f16_r64",
-             5: "accumulate_bf16"}[args.config]
-    if w.schedule == "per-backward":
-        kname = "reduce_add_mean_bf16_r16"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_GBPS, 4),
                 "traffic": traffic_record(f"{kname}__{WORKLOAD_TAG[args.config]}"),
@@ -660,8 +727,14 @@ def main():
                    "parallelism": "1 GPU (owner shard; no collectives)"},
         "gbps": round(gbps_step, 1), "frac_of_peak": round(gbps_step / PEAK_GBPS, 4),
         "overflow_steps": overflow_steps, "wall_s": round(wall, 3),
+        "step_ms": step_stats(step_ms),
         "roofline": roofline,
     }
+    if ceil:
+        line["ceiling"] = with_ceiling(roofline, ceil)
+    if args.config == 4:  # updating and skipped (overflow) steps separately, and the 4-step cycle
+        line["step_ms_update"] = step_stats([t for t, ok in zip(step_ms, launched) if ok])
+        line["step_ms_overflow"] = step_stats([t for t, ok in zip(step_ms, launched) if not ok])
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -25,9 +25,7 @@
  *     gives a message (thread-local, valid until the next call on the thread).
  *     No exceptions escape, nothing exits the process.
  *   - The caller owns every buffer.  The library allocates no memory and
- *     keeps no state between calls apart from two read-only caches: the
- *     compute-unit count of each device and the occupancy of each kernel
- *     (filled on first use).  Arguments are validated before anything is
+ *     keeps no state between calls.  Arguments are validated before anything is
  *     launched; a call that fails validation launches nothing and writes
  *     nothing.  Buffer extents cannot be seen through plain pointers: the
  *     caller guarantees the sizes stated for each argument.
@@ -66,8 +64,6 @@ enum zero_dtype {
 
 /* Most rank buffers one reduce can read (pointers travel as kernel arguments). */
 #define ZERO_MAX_RANKS 256
-/* Workspace bytes the squared-norm / overflow reduction needs (per-block partials). */
-#define ZERO_CHECK_WS_BYTES 65536
 
 /* Message for the last failed call on this thread ("" if none). */
 const char *zero_last_error(void);
@@ -172,8 +168,9 @@ int zero_state_bytes(uint64_t params, uint64_t ranks, uint32_t param_bytes, uint
  * out         device fp32, at least begin + n - out_base elements
  * d_overflow, d_sumsq: both NULL, or both device pointers; then the pass also
  *             computes the overflow flag and squared norm of the values it
- *             writes, exactly as zero_grad_check does (needs `workspace`,
- *             device, ZERO_CHECK_WS_BYTES bytes, 256-byte aligned).
+ *             writes, exactly as zero_grad_check does (needs `workspace`:
+ *             device, 256-byte aligned, at least zero_check_workspace_bytes(n)
+ *             bytes).
  * n == 0 launches nothing (the check outputs are then left untouched).
  * Errors: EINVAL (R out of [1, ZERO_MAX_RANKS], bad dtype, misaligned pointer
  *         or base, begin below a base, divisor not finite and > 0, accumulate
@@ -185,17 +182,29 @@ int zero_reduce_owned(const void *const *rank_grads, uint32_t R, int grad_dtype,
                       size_t ws_bytes, hipStream_t stream);
 
 /* ----------------------------------------------------------------------------
+ * zero_check_workspace_bytes -- device workspace a check over n elements needs
+ * (zero_grad_check, or zero_reduce_owned with the check outputs): the
+ * per-block partial sums and flags of the first stage (one block per 2048
+ * elements) and of the fold after it.  Host only; grows linearly with n
+ * (about 6 bytes per 1000 elements).
+ * Errors: EINVAL (bytes NULL).
+ * -------------------------------------------------------------------------- */
+int zero_check_workspace_bytes(uint64_t n, uint64_t *bytes);
+
+/* ----------------------------------------------------------------------------
  * zero_grad_check -- overflow flag and squared norm of an fp32 gradient.
  *
  * *d_overflow = 1 if any g[i] is infinite or NaN, else 0.
  * *d_sumsq    = sum of g[i]^2, each square and the sum in fp64 (a fixed
  *               reduction tree: per-thread sums, wavefront shuffles, an LDS
- *               block stage, then one block over the per-block partials), so
- *               the result is identical run to run on one device.  When the
+ *               block stage, then the per-block partials folded in fixed
+ *               contiguous slices), so the result is identical run to run on
+ *               one device.  When the
  *               flag is set the sum is meaningless.
  * The pages name no overflow handling; with a loss scale the caller skips the
  * step when the flag is set, and clips with zero_clip_coef otherwise.
- * g          device fp32 [n];  workspace: device, ZERO_CHECK_WS_BYTES bytes.
+ * g          device fp32 [n];  workspace: device, 256-byte aligned, at least
+ *            zero_check_workspace_bytes(n) bytes (per-block partials).
  * n == 0 writes flag 0 and sum 0.
  * Errors: EINVAL (NULL outputs, workspace too small, misaligned); EHIP.
  * -------------------------------------------------------------------------- */
@@ -239,7 +248,9 @@ typedef struct {
   int32_t adamw; /* 1: decoupled decay (AdamW); 0: classic Adam, wd added to g */
   uint64_t step;
   double clip_coef; /* 1.0 when not clipping */
-  uint32_t grid_blocks; /* 0: the library picks the persistent grid */
+  uint32_t grid_blocks; /* 0: one block per chunk (the library default); else
+                           that many blocks, each taking chunks with a grid
+                           stride (same results for every grid) */
 } zero_adam_args;
 
 /* ----------------------------------------------------------------------------
@@ -342,7 +353,7 @@ int zero3_partition_spans(const uint64_t *numel, uint32_t n_tensors, uint32_t ra
 
 /* ----------------------------------------------------------------------------
  * zero_copy_spans -- dst[span.dst + i] = srcs[span.buf][span.src + i] for every
- * span of a device span table, in one persistent multi-span launch.  The
+ * span of a device span table, in one multi-span launch.  The
  * device side of the stage-3 gather (and partition) on one GPU.
  * spans[n_spans]      device table (from the builders above)
  * srcs, src_numel     host arrays [n_srcs] of device pointers and their
@@ -356,6 +367,32 @@ int zero3_partition_spans(const uint64_t *numel, uint32_t n_tensors, uint32_t ra
 int zero_copy_spans(const zero_copy_span *spans, uint64_t n_spans, const void *const *srcs,
                     const uint64_t *src_numel, uint32_t n_srcs, void *dst, uint64_t dst_numel,
                     uint32_t elem_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------------------------
+ * Measurement.
+ * -------------------------------------------------------------------------- */
+
+/* Most source (and most destination) streams of one zero_stream_probe call. */
+#define ZERO_MAX_PROBE_STREAMS 64
+
+/* ----------------------------------------------------------------------------
+ * zero_stream_probe -- the bandwidth probe against which the optimizer kernels
+ * are measured (no part of the optimizer step; the pages define no such
+ * operation).  Every destination receives the bytewise XOR of all sources:
+ * dsts[d][i] = srcs[0][i] ^ ... ^ srcs[n_src-1][i] for i < bytes, streamed
+ * with 16-byte loads and stores in per-wavefront contiguous tiles, so one
+ * launch moves (n_src + n_dst) * bytes bytes of HBM traffic.  With one source
+ * and one destination it is a plain copy.
+ * srcs[n_src], dsts[n_dst]  host arrays of device pointers, each 16-byte
+ *                           aligned; 1 <= n_src, n_dst <= ZERO_MAX_PROBE_STREAMS
+ * bytes                     bytes per stream, a multiple of 16 (0: no launch)
+ * A destination that overlaps a source or another destination gives
+ * unspecified contents (no fault: every access stays inside the streams).
+ * Errors: EINVAL (stream counts, NULL or misaligned pointers, bytes not a
+ * multiple of 16); EHIP.
+ * -------------------------------------------------------------------------- */
+int zero_stream_probe(const void *const *srcs, uint32_t n_src, void *const *dsts, uint32_t n_dst,
+                      uint64_t bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -171,6 +171,34 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
                                ct.c_void_p(0x4000), ct.c_void_p(0x10000), 100,
                                None) == zs.ZERO_EINVAL  # workspace too small
     assert L.zero_grad_check(None, 0, None, None, None, 0, None) == zs.ZERO_EINVAL
+    # a workspace one byte short of what the query reports is rejected
+    ov, ss, ws = ct.c_void_p(0x3000), ct.c_void_p(0x4000), ct.c_void_p(0x10000)
+    for n in (1, 5000, 9_000_003):
+        need = zs.check_workspace_bytes(n)
+        assert L.zero_grad_check(ct.c_void_p(0x20000), n, ov, ss, ws, need - 1, None) == zs.ZERO_EINVAL
+        assert b"workspace" in L.zero_last_error()
+    # bandwidth probe: stream counts, byte size, NULL and misaligned pointers
+    two = (ct.c_void_p * 2)(0x1000, 0x2000)
+    assert L.zero_stream_probe(two, 0, two, 1, 64, None) == zs.ZERO_EINVAL
+    assert L.zero_stream_probe(two, 1, two, 65, 64, None) == zs.ZERO_EINVAL
+    assert L.zero_stream_probe(two, 1, two, 1, 24, None) == zs.ZERO_EINVAL
+    assert L.zero_stream_probe(None, 1, two, 1, 64, None) == zs.ZERO_EINVAL
+    assert L.zero_stream_probe(bad, 1, two, 1, 64, None) == zs.ZERO_EINVAL
+    assert L.zero_stream_probe((ct.c_void_p * 1)(0), 1, two, 1, 64, None) == zs.ZERO_EINVAL
+    assert L.zero_stream_probe(two, 1, two, 1, 0, None) == zs.ZERO_OK  # nothing to move
+
+
+def test_check_workspace_grows_with_the_block_count():
+    """One first-stage (sum, flag) pair per 2048 elements plus the fold's pairs,
+    rounded to 256 bytes; monotone in n."""
+    prev = 0
+    for n in (0, 1, 2047, 2048, 2049, 16_383, 16_384, 8_388_608, 8_390_660, 1_093_750_000):
+        b = zs.check_workspace_bytes(n)
+        parts = n // 8 // 256 + 1
+        assert b == -(-parts * 12 // 256) * 256 + 256 * 12
+        assert b >= prev
+        prev = b
+    assert zs.lib().zero_check_workspace_bytes(5, None) == zs.ZERO_EINVAL
 
 
 def test_stage3_storage_matches_oracle_and_printed_example():

@@ -102,9 +102,9 @@ def test_negative_zero_and_specials():
     assert_bits_equal(from_dev(out), oracle.reduce(rows, F32, 1.0), "specials")
 
 
-def _check_bufs():
+def _check_bufs(n=1 << 24):
     return (torch.zeros(1, dtype=torch.int32, device=DEV), torch.zeros(1, dtype=torch.float64, device=DEV),
-            zs.check_workspace(DEV))
+            zs.check_workspace(n, DEV))
 
 
 @pytest.mark.parametrize("code", [F16, BF16])
@@ -148,10 +148,28 @@ def test_overflow_flag_positions(pos, kind):
     assert int(ov.item()) == oracle.grad_check(want)[0] == 1
 
 
-@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 1000, 65_537, 1_000_003])
+def test_reduce_fused_check_two_stage_fold():
+    """A reduce with the fused check over more first-stage blocks than one fold
+    block takes (9,000,003 elements from a misaligned begin)."""
+    R, begin, n = 2, 3, 9_000_003
+    grads = _rank_inputs(F16, R, begin + n, seed=8, scale=65.536)
+    dgr = [to_dev(g, F16) for g in grads]
+    ov, ss, ws = _check_bufs(n)
+    out = torch.empty(begin + n, dtype=torch.float32, device=DEV)
+    zs.zero_reduce_owned(dgr, begin, n, float(R) * 65536, out, check=(ov, ss, ws))
+    want = oracle.reduce([g[begin:] for g in grads], F16, float(R) * 65536)
+    assert_bits_equal(from_dev(out)[begin:], want, "reduce, two-stage check")
+    flag, sumsq = oracle.grad_check(want)
+    assert int(ov.item()) == flag == 0
+    assert math.isclose(ss.item(), sumsq, rel_tol=1e-9, abs_tol=0.0)
+
+
+# 8,390,660 and 20,000,001 elements give more than 4096 first-stage blocks,
+# which are folded in two stages.
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 1000, 65_537, 1_000_003, 8_390_660, 20_000_001])
 def test_grad_check_standalone(n):
     g = gen(5, synth.STREAM_GRAD, max(n, 1), synth.DIST_NORMAL, 1e-3, F32)[:n]
-    ov, ss, ws = _check_bufs()
+    ov, ss, ws = _check_bufs(max(n, 1))
     ov.fill_(9)
     ss.fill_(-1)
     zs.zero_grad_check(to_dev(g, F32) if n else torch.empty(0, dtype=torch.float32, device=DEV),

@@ -1,0 +1,46 @@
+"""The bandwidth probe on the GPU: every destination holds the bytewise XOR of
+the sources, for one to many streams and sizes that span several tiles, a
+ragged last tile and a single vector.  Expected values are numpy XORs of the
+host copies of the sources."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import zero_sharded_optimizer_owned_amd as zs  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    zs.lib()
+    yield
+
+
+@pytest.mark.parametrize("n_src,n_dst,n_vec", [(1, 1, 1), (1, 1, 64 * 4 * 3 + 5), (3, 2, 100_003),
+                                               (10, 7, 70_001), (33, 1, 9_999), (64, 64, 517)])
+def test_probe_writes_xor_of_sources(n_src, n_dst, n_vec):
+    rng = np.random.default_rng(n_src * 1000 + n_vec)
+    host = [rng.integers(0, 2 ** 32, size=4 * n_vec, dtype=np.uint32) for _ in range(n_src)]
+    srcs = [torch.from_numpy(h.view(np.int32)).to("cuda") for h in host]
+    dsts = [torch.full((4 * n_vec + 8,), -7, dtype=torch.int32, device="cuda") for _ in range(n_dst)]
+    views = [d[:4 * n_vec] for d in dsts]
+    zs.zero_stream_probe(srcs, views)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(np.stack(host), axis=0) if n_src > 1 else host[0]
+    for d in dsts:
+        got = d.cpu().numpy().view(np.uint32)
+        assert np.array_equal(got[:4 * n_vec], want)
+        assert np.all(got[4 * n_vec:].view(np.int32) == -7)  # nothing past the streams
+
+
+def test_probe_rejects_mismatched_sizes():
+    a = torch.zeros(64, dtype=torch.int32, device="cuda")
+    b = torch.zeros(68, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        zs.zero_stream_probe([a], [b])
+    c = torch.zeros(68, dtype=torch.int32, device="cuda")
+    with pytest.raises(zs.ZeroShardError):
+        zs.zero_stream_probe([b[1:65]], [c[1:65]])  # 16-byte alignment

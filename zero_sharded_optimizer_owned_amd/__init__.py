@@ -26,16 +26,17 @@ from .build import LIB_PATH, build
 ZERO_OK, ZERO_EINVAL, ZERO_ERANGE, ZERO_EHIP = 0, -1, -2, -3
 ZERO_NONE, ZERO_F16, ZERO_BF16, ZERO_F32 = 0, 1, 2, 3
 ZERO_MAX_RANKS = 256
-ZERO_CHECK_WS_BYTES = 65536
 
 EXPORTED = ("zero_last_error", "zero_shard_layout", "zero_chunk_table", "zero_state_bytes",
             "zero_reduce_owned", "zero_grad_check", "zero_clip_coef", "zero_adam_step",
             "zero_owner_to_dense", "zero_dense_to_owner", "zero3_storage", "zero3_gather_spans",
-            "zero3_partition_spans", "zero_copy_spans")
+            "zero3_partition_spans", "zero_copy_spans", "zero_stream_probe",
+            "zero_check_workspace_bytes")
 
 CHUNK_DTYPE = np.dtype([("flat", "<u8"), ("len", "<u4"), ("tensor", "<u4")])
 SPAN_DTYPE = np.dtype([("src", "<u8"), ("dst", "<u8"), ("len", "<u4"), ("buf", "<u4")])
 ZERO_MAX_COPY_SOURCES = 128
+ZERO_MAX_PROBE_STREAMS = 64
 
 
 class ZeroShardError(RuntimeError):
@@ -87,6 +88,8 @@ def load(path: str):
     L.zero3_gather_spans.argtypes = [P, U32, U32, P, U32, U32, P, U64, P]
     L.zero3_partition_spans.argtypes = [P, U32, U32, U32, U32, P, U64, P]
     L.zero_copy_spans.argtypes = [P, U64, P, P, U32, P, U64, U32, P]
+    L.zero_stream_probe.argtypes = [P, U32, P, U32, U64, P]
+    L.zero_check_workspace_bytes.argtypes = [U64, P]
     return L
 
 
@@ -207,8 +210,8 @@ def zero_reduce_owned(rank_grads, begin: int, n: int, divisor: float, out, *, gr
     ``accumulate``: 0 ``out = sum/D``; 1 (or True) ``out = (out + sum)/D``;
     2 ``out = out + sum/D`` (per-backward reduce-and-accumulate).
 
-    ``check`` = (overflow int32[1], sumsq float64[1], workspace uint8[>=64 KiB]) device
-    tensors to also compute the overflow flag and squared norm in the same pass.
+    ``check`` = (overflow int32[1], sumsq float64[1], workspace uint8[>= check_workspace_bytes(n)])
+    device tensors to also compute the overflow flag and squared norm in the same pass.
     """
     torch = _torch()
     arr, code = _rank_ptrs(rank_grads, grad_base, begin + n)
@@ -242,10 +245,17 @@ def zero_grad_check(g, overflow, sumsq, workspace) -> None:
         workspace.numel() * workspace.element_size(), _stream()))
 
 
-def check_workspace(device=None):
-    """A device buffer of ZERO_CHECK_WS_BYTES bytes for the overflow / norm reduction."""
+def check_workspace_bytes(n: int) -> int:
+    """Bytes of device workspace a check over n elements needs."""
+    out = np.zeros(1, dtype=np.uint64)
+    _check(lib().zero_check_workspace_bytes(n, _p(out)))
+    return int(out[0])
+
+
+def check_workspace(n: int, device=None):
+    """A device buffer for the overflow / norm reduction over n elements."""
     torch = _torch()
-    return torch.empty(ZERO_CHECK_WS_BYTES, dtype=torch.uint8, device=device or "cuda")
+    return torch.empty(check_workspace_bytes(n), dtype=torch.uint8, device=device or "cuda")
 
 
 def chunks_to_device(chunks: np.ndarray, device=None):
@@ -397,6 +407,25 @@ def zero_copy_spans(spans_dev, n_spans: int, srcs, dst) -> None:
     _check(lib().zero_copy_spans(ct.c_void_p(spans_dev.data_ptr()) if spans_dev is not None else None,
                                  n_spans, arr, _p(sizes), len(srcs), ct.c_void_p(dst.data_ptr()),
                                  dst.numel(), dst.element_size(), _stream()))
+
+
+def zero_stream_probe(srcs, dsts) -> None:
+    """Bandwidth probe: every destination gets the bytewise XOR of all sources.
+
+    All tensors are contiguous device tensors of one byte size (a multiple of
+    16); one launch moves (len(srcs) + len(dsts)) * that many bytes.
+    """
+    if not 1 <= len(srcs) <= ZERO_MAX_PROBE_STREAMS or not 1 <= len(dsts) <= ZERO_MAX_PROBE_STREAMS:
+        raise ValueError(f"between 1 and {ZERO_MAX_PROBE_STREAMS} sources and destinations")
+    nbytes = srcs[0].numel() * srcs[0].element_size()
+    sa, da = (ct.c_void_p * len(srcs))(), (ct.c_void_p * len(dsts))()
+    for arr, ts, name in ((sa, srcs, "srcs"), (da, dsts, "dsts")):
+        for i, t in enumerate(ts):
+            _dev(t, f"{name}[{i}]")
+            if t.numel() * t.element_size() != nbytes:
+                raise ValueError("all probe streams must have the same byte size")
+            arr[i] = t.data_ptr()
+    _check(lib().zero_stream_probe(sa, len(srcs), da, len(dsts), nbytes, _stream()))
 
 
 # ---------------------------------------------------------------- convenience

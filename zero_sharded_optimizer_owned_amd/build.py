@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libzero_shard.so")
-SOURCES = ("host.cpp", "launch.hip", "step.hip", "copy.hip")
+SOURCES = ("host.cpp", "launch.hip", "step.hip", "copy.hip", "probe.hip")
 # The sources whose kernels make up the optimizer step (hashed to tie counter
 # records to the code they were taken on).
 STEP_SOURCES = ("step.hip", "launch.hip", "launch.h", "internal.h")

@@ -29,29 +29,25 @@ struct DenseArgs {
   uint64_t dense_total;
 };
 
-// Each wavefront copies whole chunks, 64 consecutive elements per instruction
-// on both sides, four instructions in flight per lane.  Chunks whose tensor
-// index or position disagrees with the tables are skipped, and no dense
-// index at or past dense_total is touched.
+// One block per chunk (grid stride past the grid): consecutive threads copy
+// consecutive elements on both sides, four per thread in flight.  Chunks
+// whose tensor index or position disagrees with the tables are skipped, and
+// no dense index at or past dense_total is touched.
 template <bool TO_DENSE>
 __global__ void __launch_bounds__(kBlock) dense_kernel(const DenseArgs a) {
-  const uint64_t lane = threadIdx.x & 63;
-  const uint64_t wave =
-      __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-  const uint64_t n_waves = (uint64_t)gridDim.x * kWavesPerBlock;
-  for (uint64_t c = wave; c < a.n_chunks; c += n_waves) {
+  for (uint64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
     const zero_chunk ch = a.chunks[c];
     if (ch.tensor >= a.n_tensors) continue;
     const uint64_t toff = a.tensor_offset[ch.tensor];
     const uint64_t doff = a.dense_offset[ch.tensor];
     const uint64_t f0 = max(max(ch.flat, a.begin), toff);
     const uint64_t f1 = min(ch.flat + ch.len, a.end);
-    for (uint64_t f = f0 + lane; f < f1; f += 256) {
+    for (uint64_t f = f0 + threadIdx.x; f < f1; f += 4 * kBlock) {
       float x[4];
       uint64_t d[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint64_t fj = f + 64 * j;
+        const uint64_t fj = f + kBlock * j;
         d[j] = fj < f1 ? doff + (fj - toff) : a.dense_total;
         if (d[j] < a.dense_total) x[j] = TO_DENSE ? a.owner[fj - a.owner_base] : a.dense[d[j]];
       }
@@ -59,7 +55,7 @@ __global__ void __launch_bounds__(kBlock) dense_kernel(const DenseArgs a) {
       for (int j = 0; j < 4; ++j) {
         if (d[j] < a.dense_total) {
           if (TO_DENSE) a.dense[d[j]] = x[j];
-          else a.owner[f + 64 * j - a.owner_base] = x[j];
+          else a.owner[f + kBlock * j - a.owner_base] = x[j];
         }
       }
     }
@@ -79,19 +75,16 @@ struct SpanArgs {
   uint64_t dst_numel;
 };
 
-// One wavefront per span (grid stride over the table).  When source and
+// One block per span (grid stride past the grid).  When source and
 // destination share their phase within a 16-byte vector, the body moves as
-// 128-bit vectors (four per lane in flight) between scalar head and tail
-// pieces; otherwise lanes copy single elements, four per lane in flight.
-// Spans that do not fit their buffers are skipped.
+// 128-bit vectors (consecutive threads on consecutive vectors, up to four per
+// thread in flight) between scalar head and tail pieces; otherwise threads
+// copy single elements.  Spans that do not fit their buffers are skipped.
 template <typename T>
 __global__ void __launch_bounds__(kBlock) span_kernel(const SpanArgs a) {
   constexpr uint64_t V = 16 / sizeof(T);
-  const uint64_t lane = threadIdx.x & 63;
-  const uint64_t wave =
-      __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-  const uint64_t n_waves = (uint64_t)gridDim.x * kWavesPerBlock;
-  for (uint64_t c = wave; c < a.n_spans; c += n_waves) {
+  const uint64_t t = threadIdx.x;
+  for (uint64_t c = blockIdx.x; c < a.n_spans; c += gridDim.x) {
     const zero_copy_span sp = a.spans[c];
     if (sp.buf >= a.n_srcs) continue;
     const uint64_t len = sp.len;
@@ -103,28 +96,28 @@ __global__ void __launch_bounds__(kBlock) span_kernel(const SpanArgs a) {
       const uint64_t head = min(len, (V - sp.dst % V) % V);
       const uint64_t body = (len - head) / V;
       const uint64_t tail0 = head + body * V;
-      if (lane < head) d[lane] = s[lane];
-      if (lane < len - tail0) d[tail0 + lane] = s[tail0 + lane];
+      if (t < head) d[t] = s[t];
+      if (t < len - tail0) d[tail0 + t] = s[tail0 + t];
       const uint4* sv = reinterpret_cast<const uint4*>(s + head);
       uint4* dv = reinterpret_cast<uint4*>(d + head);
-      for (uint64_t v = lane; v < body; v += 256) {
+      for (uint64_t v = t; v < body; v += 4 * kBlock) {
         uint4 x[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (v + 64 * j < body) x[j] = sv[v + 64 * j];
+          if (v + kBlock * j < body) x[j] = sv[v + kBlock * j];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (v + 64 * j < body) dv[v + 64 * j] = x[j];
+          if (v + kBlock * j < body) dv[v + kBlock * j] = x[j];
       }
     } else {
-      for (uint64_t i = lane; i < len; i += 256) {
+      for (uint64_t i = t; i < len; i += 4 * kBlock) {
         T x[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (i + 64 * j < len) x[j] = s[i + 64 * j];
+          if (i + kBlock * j < len) x[j] = s[i + kBlock * j];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (i + 64 * j < len) d[i + 64 * j] = x[j];
+          if (i + kBlock * j < len) d[i + kBlock * j] = x[j];
       }
     }
   }
@@ -149,8 +142,7 @@ int dense_copy(bool to_dense, const zero_chunk* chunks, uint64_t n_chunks, uint6
   if ((reinterpret_cast<uintptr_t>(owner) | reinterpret_cast<uintptr_t>(dense)) & 3u)
     return fail(ZERO_EINVAL, "%s: fp32 buffers must be 4-byte aligned", who);
   if (n_chunks == 0 || begin == end) return ZERO_OK;
-  int cus = 0;
-  int rc = begin_launch(&cus);
+  int rc = begin_launch();
   if (rc) return rc;
   DenseArgs a;
   a.chunks = chunks;
@@ -164,15 +156,8 @@ int dense_copy(bool to_dense, const zero_chunk* chunks, uint64_t n_chunks, uint6
   a.owner_base = owner_base;
   a.dense = dense;
   a.dense_total = dense_total;
-  if (to_dense) {
-    static const uint32_t per_cu = blocks_per_cu(dense_kernel<true>);
-    hipLaunchKernelGGL(dense_kernel<true>, persistent_grid(per_cu, n_chunks, cus, 0), kBlock, 0,
-                       stream, a);
-  } else {
-    static const uint32_t per_cu = blocks_per_cu(dense_kernel<false>);
-    hipLaunchKernelGGL(dense_kernel<false>, persistent_grid(per_cu, n_chunks, cus, 0), kBlock, 0,
-                       stream, a);
-  }
+  if (to_dense) hipLaunchKernelGGL(dense_kernel<true>, chunk_grid(n_chunks, 0), kBlock, 0, stream, a);
+  else hipLaunchKernelGGL(dense_kernel<false>, chunk_grid(n_chunks, 0), kBlock, 0, stream, a);
   return launch_status(who);
 }
 }  // namespace
@@ -222,17 +207,11 @@ extern "C" int zero_copy_spans(const zero_copy_span* spans, uint64_t n_spans, co
   a.n_srcs = n_srcs;
   a.dst = dst;
   a.dst_numel = dst_numel;
-  int cus = 0;
-  int rc = begin_launch(&cus);
+  int rc = begin_launch();
   if (rc) return rc;
-  if (elem_bytes == 2) {
-    static const uint32_t per_cu = blocks_per_cu(span_kernel<uint16_t>);
-    hipLaunchKernelGGL(span_kernel<uint16_t>, persistent_grid(per_cu, n_spans, cus, 0), kBlock, 0,
-                       stream, a);
-  } else {
-    static const uint32_t per_cu = blocks_per_cu(span_kernel<uint32_t>);
-    hipLaunchKernelGGL(span_kernel<uint32_t>, persistent_grid(per_cu, n_spans, cus, 0), kBlock, 0,
-                       stream, a);
-  }
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(span_kernel<uint16_t>, chunk_grid(n_spans, 0), kBlock, 0, stream, a);
+  else
+    hipLaunchKernelGGL(span_kernel<uint32_t>, chunk_grid(n_spans, 0), kBlock, 0, stream, a);
   return launch_status(who);
 }

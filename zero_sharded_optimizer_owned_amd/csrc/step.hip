@@ -33,14 +33,10 @@
 namespace zs {
 namespace {
 
-constexpr int kMaxPartials = 4096;  // per-block partials the check workspace holds
-// Flat-range kernels hand out work in tiles: one wavefront streams a contiguous
-// span of every stream (up to 512 vectors = 4096 elements) before taking the
-// next tile with a grid stride.  Short ranges use shorter tiles (down to one
-// vector per lane) so that every CU still gets work.
-constexpr uint64_t kMaxTileVectors = 512;
-static_assert(kMaxPartials * (sizeof(double) + sizeof(int32_t)) <= ZERO_CHECK_WS_BYTES,
-              "check workspace too small");
+// The check's per-block partials are folded by one block when there are at
+// most kFoldDirect of them, else first by kFinalBlocks blocks.
+constexpr uint64_t kFoldDirect = 4096;
+constexpr uint64_t kFinalBlocks = 256;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
@@ -296,8 +292,10 @@ __device__ __forceinline__ void check_accum(float g, double& sq, int& bad) {
 }
 
 struct CheckOut {
-  double* partial;  // [gridDim.x]
-  int32_t* flags;   // [gridDim.x]
+  double* partial;   // [parts] one per block of the first stage
+  int32_t* flags;    // [parts]
+  double* partial2;  // [kFinalBlocks] second stage (large part counts)
+  int32_t* flags2;   // [kFinalBlocks]
 };
 
 // ---------------------------------------------------------------------------
@@ -306,7 +304,7 @@ struct CheckOut {
 struct ReduceArgs {
   RankSet rs;
   uint64_t begin, end;
-  uint64_t tile;  // vectors per wavefront tile
+  uint64_t piece;  // vectors per block piece, a multiple of kBlock
   float* out;
   uint64_t out_base;
   CheckOut chk;
@@ -319,6 +317,11 @@ enum AccumMode : int {
   kAddMean = 2         // out = out + sum / D   (per-backward reduce, then accumulate)
 };
 
+// Flat-range kernels split the range into pieces of `piece` vectors: block b
+// takes piece b, its threads on consecutive 128-bit vectors of every stream,
+// so a block streams one short contiguous piece of each stream and exits, and
+// blocks are dispatched in order.  A grid smaller than the piece count (only
+// for ranges beyond kMaxChunkGrid pieces) takes the rest with a grid stride.
 template <int DT, int MODE, bool CHECK>
 __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs a) {
   const uint64_t f0 = a.begin, f1 = a.end;
@@ -340,12 +343,10 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs a) {
     }
   }
   const uint64_t v0 = a0 / 8, n_vec = a1 / 8 - v0;
-  const uint64_t lane = threadIdx.x & 63;
-  const uint64_t wave = (uint64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  const uint64_t n_waves = (uint64_t)gridDim.x * kWavesPerBlock;
-  for (uint64_t t0 = wave * a.tile; t0 < n_vec; t0 += n_waves * a.tile) {
-    const uint64_t t1 = min(n_vec, t0 + a.tile);
-    for (uint64_t v = t0 + lane; v < t1; v += 64) {
+  const uint64_t stride = (uint64_t)gridDim.x * a.piece;
+  for (uint64_t p0 = (uint64_t)blockIdx.x * a.piece; p0 < n_vec; p0 += stride) {
+    const uint64_t p1 = min(n_vec, p0 + a.piece);
+    for (uint64_t v = p0 + threadIdx.x; v < p1; v += kBlock) {
       const uint64_t f[1] = {(v0 + v) * 8};
       float s[1][8], old[8];
       if (MODE == kStartFromOut) {
@@ -377,26 +378,20 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// K2: check of a stored fp32 gradient (first stage), and the final stage.
+// K2: check of a stored fp32 gradient (first stage), and the final stages.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kBlock) check_kernel(const float* g, uint64_t n, uint64_t tile,
-                                                       CheckOut chk) {
+__global__ void __launch_bounds__(kBlock) check_kernel(const float* g, uint64_t n, CheckOut chk) {
   const uint64_t a1 = n & ~7ull;
   double sq = 0.0;
   int bad = 0;
   if (blockIdx.x == 0 && threadIdx.x < n - a1) check_accum(g[a1 + threadIdx.x], sq, bad);
   const uint64_t n_vec = a1 / 8;
-  const uint64_t lane = threadIdx.x & 63;
-  const uint64_t wave = (uint64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  const uint64_t n_waves = (uint64_t)gridDim.x * kWavesPerBlock;
-  for (uint64_t t0 = wave * tile; t0 < n_vec; t0 += n_waves * tile) {
-    const uint64_t t1 = min(n_vec, t0 + tile);
-    for (uint64_t v = t0 + lane; v < t1; v += 64) {
-      float x[8];
-      load8f(g, v * 8, x);
+  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
+  for (uint64_t v = (uint64_t)blockIdx.x * kBlock + threadIdx.x; v < n_vec; v += stride) {
+    float x[8];
+    load8f(g, v * 8, x);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) check_accum(x[k], sq, bad);
-    }
+    for (int k = 0; k < 8; ++k) check_accum(x[k], sq, bad);
   }
   block_reduce(sq, bad);
   if (threadIdx.x == 0) {
@@ -405,18 +400,25 @@ __global__ void __launch_bounds__(kBlock) check_kernel(const float* g, uint64_t 
   }
 }
 
-__global__ void __launch_bounds__(kBlock) check_final_kernel(CheckOut chk, uint32_t parts,
-                                                             int32_t* d_overflow, double* d_sumsq) {
+// Folds parts (sum, any) pairs: block b takes the contiguous slice
+// [b * per, min(parts, (b + 1) * per)) in a fixed order and writes its result
+// to (out_sum[b], out_flag[b]).  The same part count always gives the same
+// tree, so the result is identical run to run.
+__global__ void __launch_bounds__(kBlock) check_fold_kernel(const double* sum, const int32_t* flag,
+                                                            uint64_t parts, uint64_t per,
+                                                            double* out_sum, int32_t* out_flag) {
+  const uint64_t lo = (uint64_t)blockIdx.x * per;
+  const uint64_t hi = min(parts, lo + per);
   double sq = 0.0;
   int bad = 0;
-  for (uint32_t i = threadIdx.x; i < parts; i += kBlock) {
-    sq = sq + chk.partial[i];
-    bad |= chk.flags[i];
+  for (uint64_t i = lo + threadIdx.x; i < hi; i += kBlock) {
+    sq = sq + sum[i];
+    bad |= flag[i];
   }
   block_reduce(sq, bad);
   if (threadIdx.x == 0) {
-    *d_sumsq = sq;
-    *d_overflow = bad ? 1 : 0;
+    out_sum[blockIdx.x] = sq;
+    out_flag[blockIdx.x] = bad ? 1 : 0;
   }
 }
 
@@ -534,44 +536,39 @@ __device__ __forceinline__ void adam_one(const AdamArgs& a, uint64_t f) {
   if constexpr (PDT != ZERO_NONE) Elem<PDT>::store1(a.p16, f - a.param_base, w);
 }
 
-// Persistent multi-tensor kernel: wavefront `wave` takes chunks wave,
-// wave + n_waves, ...; the next chunk's descriptor is fetched while the
-// current chunk streams.
+// Multi-tensor kernel, one block per chunk: the block's threads take the
+// chunk's 128-bit vectors in order (thread t on vectors t, t + kBlock, ...),
+// so a block streams one short contiguous piece of every stream and exits.
+// Blocks are dispatched in chunk order, which keeps the pieces in flight
+// across the chip inside a narrow window of each stream.  A grid smaller than
+// the chunk count takes the remaining chunks with a grid stride.
 template <int GDT, int PDT, int RC>
 __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs a) {
   constexpr int U = StepUnroll<GDT, RC>::value;
-  const uint32_t lane = threadIdx.x & 63;
-  const uint64_t wave =
-      __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-  const uint64_t n_waves = (uint64_t)gridDim.x * kWavesPerBlock;
-  if (wave >= a.n_chunks) return;
-  zero_chunk ch = a.chunks[wave];
-  for (uint64_t c = wave; c < a.n_chunks; c += n_waves) {
-    zero_chunk next = ch;
-    if (c + n_waves < a.n_chunks) next = a.chunks[c + n_waves];
+  const uint32_t t = threadIdx.x;
+  for (uint64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
+    const zero_chunk ch = a.chunks[c];
     const uint64_t f0 = max(ch.flat, a.begin);
     const uint64_t f1 = min(ch.flat + ch.len, a.end);
-    if (f0 < f1) {
-      const uint64_t a0 = min(f1, (f0 + 7) & ~7ull);
-      const uint64_t a1 = max(a0, f1 & ~7ull);
-      // Scalar peels: lanes 0-6 take the head before the first vector
-      // boundary, lanes 8-14 the tail after the last one.
-      if (lane < a0 - f0) adam_one<GDT, PDT, RC>(a, f0 + lane);
-      else if (lane >= 8 && lane - 8 < f1 - a1) adam_one<GDT, PDT, RC>(a, a1 + lane - 8);
-      uint64_t vi = a0 / 8 + lane;
-      const uint64_t vend = a1 / 8;
-      if constexpr (U == 2) {
-        for (; vi + 64 < vend; vi += 128) {
-          const uint64_t f[2] = {vi * 8, (vi + 64) * 8};
-          adam_vec<GDT, PDT, RC, 2>(a, f);
-        }
-      }
-      for (; vi < vend; vi += 64) {
-        const uint64_t f[1] = {vi * 8};
-        adam_vec<GDT, PDT, RC, 1>(a, f);
+    if (f0 >= f1) continue;
+    const uint64_t a0 = min(f1, (f0 + 7) & ~7ull);
+    const uint64_t a1 = max(a0, f1 & ~7ull);
+    // Scalar peels: threads 0-6 take the head before the first vector
+    // boundary, threads 8-14 the tail after the last one.
+    if (t < a0 - f0) adam_one<GDT, PDT, RC>(a, f0 + t);
+    else if (t >= 8 && t - 8 < f1 - a1) adam_one<GDT, PDT, RC>(a, a1 + t - 8);
+    uint64_t vi = a0 / 8 + t;
+    const uint64_t vend = a1 / 8;
+    if constexpr (U == 2) {
+      for (; vi + kBlock < vend; vi += 2 * kBlock) {
+        const uint64_t f[2] = {vi * 8, (vi + kBlock) * 8};
+        adam_vec<GDT, PDT, RC, 2>(a, f);
       }
     }
-    ch = next;
+    for (; vi < vend; vi += kBlock) {
+      const uint64_t f[1] = {vi * 8};
+      adam_vec<GDT, PDT, RC, 1>(a, f);
+    }
   }
 }
 
@@ -615,43 +612,62 @@ int fill_ranks(RankSet* rs, const void* const* rank_grads, uint32_t R, int dtype
   return ZERO_OK;
 }
 
-int check_workspace(void* ws, size_t ws_bytes, const char* who) {
+// Blocks of a flat-range kernel over n_vec vectors: one per piece.
+uint32_t flat_grid(uint64_t n_vec, uint64_t piece = kBlock) {
+  return chunk_grid((n_vec + piece - 1) / piece, 0);
+}
+
+// Vectors per block piece of the rank reduce: one per thread, two once the
+// ranks are many (measured: 64 fp16 ranks stream faster with 8 KiB pieces of
+// each rank, one fp16 source faster with 4 KiB pieces).
+uint64_t reduce_piece(uint32_t R) { return R >= 32 ? 2 * kBlock : kBlock; }
+
+// Workspace of a check whose first stage has `parts` blocks: the per-block
+// (sum, flag) pairs, then the second-stage pairs.
+uint64_t check_ws_bytes(uint64_t parts) {
+  const uint64_t first = (parts * (sizeof(double) + sizeof(int32_t)) + 255) / 256 * 256;
+  return first + kFinalBlocks * (sizeof(double) + sizeof(int32_t));
+}
+
+// Most first-stage blocks a check over n elements can use (any begin).
+uint64_t check_parts(uint64_t n) { return flat_grid(n / 8 + 1); }
+
+int check_workspace(void* ws, size_t ws_bytes, uint64_t n, const char* who) {
   if (!ws) return fail(ZERO_EINVAL, "%s: workspace is NULL", who);
-  if (ws_bytes < ZERO_CHECK_WS_BYTES)
-    return fail(ZERO_EINVAL, "%s: workspace needs %d bytes, got %zu", who, ZERO_CHECK_WS_BYTES,
-                ws_bytes);
+  const uint64_t need = check_ws_bytes(check_parts(n));
+  if (ws_bytes < need)
+    return fail(ZERO_EINVAL, "%s: workspace needs %llu bytes for %llu elements, got %zu", who,
+                (unsigned long long)need, (unsigned long long)n, ws_bytes);
   if (reinterpret_cast<uintptr_t>(ws) & 255u)
     return fail(ZERO_EINVAL, "%s: workspace must be 256-byte aligned", who);
   return ZERO_OK;
 }
 
-CheckOut check_layout(void* ws) {
+CheckOut check_layout(void* ws, uint64_t parts) {
+  char* b = static_cast<char*>(ws);
+  const uint64_t first = (parts * (sizeof(double) + sizeof(int32_t)) + 255) / 256 * 256;
   CheckOut c;
-  c.partial = static_cast<double*>(ws);
-  c.flags = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + kMaxPartials * sizeof(double));
+  c.partial = reinterpret_cast<double*>(b);
+  c.flags = reinterpret_cast<int32_t*>(b + parts * sizeof(double));
+  c.partial2 = reinterpret_cast<double*>(b + first);
+  c.flags2 = reinterpret_cast<int32_t*>(b + first + kFinalBlocks * sizeof(double));
   return c;
 }
 
-// Launch shape of a flat-range kernel: at most eight 256-thread blocks per CU
-// and `cap` blocks; the tile is the longest (<= 512 vectors, a multiple of 64)
-// that still gives every wavefront of that grid a tile.
-struct FlatPlan {
-  uint32_t grid;
-  uint64_t tile;
-};
-
-FlatPlan flat_plan(uint64_t n_vectors, int cus, uint32_t cap) {
-  uint64_t blocks = (uint64_t)cus * 8;
-  if (blocks > cap) blocks = cap;
-  const uint64_t waves = blocks * kWavesPerBlock;
-  uint64_t tile = (n_vectors + waves - 1) / waves;
-  tile = (tile + 63) / 64 * 64;
-  if (tile < 64) tile = 64;
-  if (tile > kMaxTileVectors) tile = kMaxTileVectors;
-  const uint64_t tiles = (n_vectors + tile - 1) / tile;
-  uint64_t want = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (want > blocks) want = blocks;
-  return FlatPlan{want == 0 ? 1u : (uint32_t)want, tile};
+// Folds the first stage's `parts` pairs into the two outputs in a fixed tree.
+void finish_check(const CheckOut& c, uint64_t parts, int32_t* d_overflow, double* d_sumsq,
+                  hipStream_t s) {
+  if (parts <= kFoldDirect) {
+    hipLaunchKernelGGL(check_fold_kernel, 1, kBlock, 0, s, c.partial, c.flags, parts, parts, d_sumsq,
+                       d_overflow);
+    return;
+  }
+  const uint64_t per = (parts + kFinalBlocks - 1) / kFinalBlocks;
+  const uint64_t blocks = (parts + per - 1) / per;
+  hipLaunchKernelGGL(check_fold_kernel, (uint32_t)blocks, kBlock, 0, s, c.partial, c.flags, parts, per,
+                     c.partial2, c.flags2);
+  hipLaunchKernelGGL(check_fold_kernel, 1, kBlock, 0, s, c.partial2, c.flags2, blocks, blocks,
+                     d_sumsq, d_overflow);
 }
 
 template <int DT, int MODE>
@@ -668,29 +684,27 @@ void launch_reduce(const ReduceArgs& a, int mode, bool check, uint32_t grid, hip
 }
 
 template <int GDT, int PDT, int RC>
-void launch_adam_k(const AdamArgs& a, int cus, uint32_t grid, hipStream_t s) {
-  const auto k = adam_kernel<GDT, PDT, RC>;
-  static const uint32_t per_cu = blocks_per_cu(k);  // one query per instantiation
-  hipLaunchKernelGGL(k, persistent_grid(per_cu, a.n_chunks, cus, grid), kBlock, 0, s, a);
+void launch_adam_k(const AdamArgs& a, uint32_t grid, hipStream_t s) {
+  hipLaunchKernelGGL((adam_kernel<GDT, PDT, RC>), chunk_grid(a.n_chunks, grid), kBlock, 0, s, a);
 }
 
 template <int GDT, int RC>
-void launch_adam_p(const AdamArgs& a, int pdt, int cus, uint32_t grid, hipStream_t s) {
-  if (pdt == ZERO_F16) launch_adam_k<GDT, ZERO_F16, RC>(a, cus, grid, s);
-  else if (pdt == ZERO_BF16) launch_adam_k<GDT, ZERO_BF16, RC>(a, cus, grid, s);
-  else launch_adam_k<GDT, ZERO_NONE, RC>(a, cus, grid, s);
+void launch_adam_p(const AdamArgs& a, int pdt, uint32_t grid, hipStream_t s) {
+  if (pdt == ZERO_F16) launch_adam_k<GDT, ZERO_F16, RC>(a, grid, s);
+  else if (pdt == ZERO_BF16) launch_adam_k<GDT, ZERO_BF16, RC>(a, grid, s);
+  else launch_adam_k<GDT, ZERO_NONE, RC>(a, grid, s);
 }
 
 // Rank counts with a fully unrolled kernel; any other count takes the batched one.
 template <int GDT>
-void launch_adam_r(const AdamArgs& a, int pdt, int cus, uint32_t grid, hipStream_t s) {
+void launch_adam_r(const AdamArgs& a, int pdt, uint32_t grid, hipStream_t s) {
   switch (a.rs.R) {
-    case 1: launch_adam_p<GDT, 1>(a, pdt, cus, grid, s); break;
-    case 2: launch_adam_p<GDT, 2>(a, pdt, cus, grid, s); break;
-    case 4: launch_adam_p<GDT, 4>(a, pdt, cus, grid, s); break;
-    case 8: launch_adam_p<GDT, 8>(a, pdt, cus, grid, s); break;
-    case 16: launch_adam_p<GDT, 16>(a, pdt, cus, grid, s); break;
-    default: launch_adam_p<GDT, 0>(a, pdt, cus, grid, s); break;
+    case 1: launch_adam_p<GDT, 1>(a, pdt, grid, s); break;
+    case 2: launch_adam_p<GDT, 2>(a, pdt, grid, s); break;
+    case 4: launch_adam_p<GDT, 4>(a, pdt, grid, s); break;
+    case 8: launch_adam_p<GDT, 8>(a, pdt, grid, s); break;
+    case 16: launch_adam_p<GDT, 16>(a, pdt, grid, s); break;
+    default: launch_adam_p<GDT, 0>(a, pdt, grid, s); break;
   }
 }
 
@@ -721,19 +735,19 @@ extern "C" int zero_reduce_owned(const void* const* rank_grads, uint32_t R, int 
   if (check) {
     if (!d_overflow || !d_sumsq)
       return fail(ZERO_EINVAL, "%s: give both d_overflow and d_sumsq, or neither", who);
-    if ((rc = check_workspace(workspace, ws_bytes, who))) return rc;
+    if ((rc = check_workspace(workspace, ws_bytes, n, who))) return rc;
   }
   if (n == 0) return ZERO_OK;
-  int cus = 0;
-  if ((rc = begin_launch(&cus))) return rc;
+  if ((rc = begin_launch())) return rc;
   a.begin = begin;
   a.end = begin + n;
   a.out = out;
   a.out_base = out_base;
-  if (check) a.chk = check_layout(workspace);
-  const FlatPlan plan = flat_plan((n + 7) / 8, cus, kMaxPartials);
-  const uint32_t grid = plan.grid;
-  a.tile = plan.tile;
+  const uint64_t a0 = std::min<uint64_t>(a.end, (begin + 7) & ~7ull);
+  const uint64_t a1 = std::max<uint64_t>(a0, a.end & ~7ull);
+  a.piece = reduce_piece(R);
+  const uint32_t grid = flat_grid(a1 / 8 - a0 / 8, a.piece);
+  if (check) a.chk = check_layout(workspace, grid);
   switch (grad_dtype) {
     case ZERO_F16: launch_reduce<ZERO_F16>(a, accumulate, check, grid, stream); break;
     case ZERO_BF16: launch_reduce<ZERO_BF16>(a, accumulate, check, grid, stream); break;
@@ -741,9 +755,16 @@ extern "C" int zero_reduce_owned(const void* const* rank_grads, uint32_t R, int 
   }
   if ((rc = launch_status(who))) return rc;
   if (check) {
-    hipLaunchKernelGGL(check_final_kernel, 1, kBlock, 0, stream, a.chk, grid, d_overflow, d_sumsq);
+    finish_check(a.chk, grid, d_overflow, d_sumsq, stream);
     if ((rc = launch_status(who))) return rc;
   }
+  return ZERO_OK;
+}
+
+extern "C" int zero_check_workspace_bytes(uint64_t n, uint64_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(ZERO_EINVAL, "zero_check_workspace_bytes: bytes is NULL");
+  *bytes = check_ws_bytes(check_parts(n));
   return ZERO_OK;
 }
 
@@ -752,18 +773,16 @@ extern "C" int zero_grad_check(const float* g, uint64_t n, int32_t* d_overflow, 
   static const char* who = "zero_grad_check";
   clear_error();
   if (!d_overflow || !d_sumsq) return fail(ZERO_EINVAL, "%s: NULL output", who);
-  int rc = check_workspace(workspace, ws_bytes, who);
+  int rc = check_workspace(workspace, ws_bytes, n, who);
   if (rc) return rc;
   if (n > 0 && !g) return fail(ZERO_EINVAL, "%s: g is NULL", who);
   if (n > 0 && !aligned16(g)) return fail(ZERO_EINVAL, "%s: g is not 16-byte aligned", who);
-  int cus = 0;
-  if ((rc = begin_launch(&cus))) return rc;
-  const FlatPlan plan = flat_plan(n / 8, cus, kMaxPartials);
-  const uint32_t grid = plan.grid;
-  const CheckOut chk = check_layout(workspace);
-  hipLaunchKernelGGL(check_kernel, grid, kBlock, 0, stream, g, n, plan.tile, chk);
+  if ((rc = begin_launch())) return rc;
+  const uint32_t grid = flat_grid(n / 8);
+  const CheckOut chk = check_layout(workspace, grid);
+  hipLaunchKernelGGL(check_kernel, grid, kBlock, 0, stream, g, n, chk);
   if ((rc = launch_status(who))) return rc;
-  hipLaunchKernelGGL(check_final_kernel, 1, kBlock, 0, stream, chk, grid, d_overflow, d_sumsq);
+  finish_check(chk, grid, d_overflow, d_sumsq, stream);
   return launch_status(who);
 }
 
@@ -808,8 +827,7 @@ extern "C" int zero_adam_step(const zero_adam_args* p, hipStream_t stream) {
   if (p->beta1 < 0 || p->beta1 >= 1 || p->beta2 < 0 || p->beta2 >= 1)
     return fail(ZERO_EINVAL, "%s: betas must lie in [0, 1)", who);
   if (p->n_chunks == 0 || p->begin == p->end) return ZERO_OK;
-  int cus = 0;
-  if ((rc = begin_launch(&cus))) return rc;
+  if ((rc = begin_launch())) return rc;
 
   // Constants in fp64, each rounded once to fp32.
   const double t = (double)p->step;
@@ -839,12 +857,12 @@ extern "C" int zero_adam_step(const zero_adam_args* p, hipStream_t stream) {
 
   const uint32_t grid = p->grid_blocks;
   if (reduced) {
-    launch_adam_p<ZERO_F32, kReduced>(a, pdt, cus, grid, stream);
+    launch_adam_p<ZERO_F32, kReduced>(a, pdt, grid, stream);
   } else {
     switch (p->grad_dtype) {
-      case ZERO_F16: launch_adam_r<ZERO_F16>(a, pdt, cus, grid, stream); break;
-      case ZERO_BF16: launch_adam_r<ZERO_BF16>(a, pdt, cus, grid, stream); break;
-      default: launch_adam_r<ZERO_F32>(a, pdt, cus, grid, stream); break;
+      case ZERO_F16: launch_adam_r<ZERO_F16>(a, pdt, grid, stream); break;
+      case ZERO_BF16: launch_adam_r<ZERO_BF16>(a, pdt, grid, stream); break;
+      default: launch_adam_r<ZERO_F32>(a, pdt, grid, stream); break;
     }
   }
   return launch_status(who);
