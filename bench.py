@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--schedule", default="accumulate", choices=("accumulate", "per-backward"),
                     help="config 5 only: accumulate microsteps locally then reduce (default), or reduce "
                          "every microstep and add the owned mean to an fp32 accumulator")
-    ap.add_argument("--grid", type=int, default=0, help="persistent grid blocks (0: library default)")
+    ap.add_argument("--grid", type=int, default=0, help="fused-step grid blocks (0: library default, one block per chunk)")
     ap.add_argument("--chunk", type=int, default=DEFAULT_CHUNK, help="max chunk elements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

@@ -380,7 +380,7 @@ int zero_copy_spans(const zero_copy_span *spans, uint64_t n_spans, const void *c
  * are measured (no part of the optimizer step; the pages define no such
  * operation).  Every destination receives the bytewise XOR of all sources:
  * dsts[d][i] = srcs[0][i] ^ ... ^ srcs[n_src-1][i] for i < bytes, streamed
- * with 16-byte loads and stores in per-wavefront contiguous tiles, so one
+ * with 16-byte loads and stores, one block per 256-vector piece, so one
  * launch moves (n_src + n_dst) * bytes bytes of HBM traffic.  With one source
  * and one destination it is a plain copy.
  * srcs[n_src], dsts[n_dst]  host arrays of device pointers, each 16-byte

@@ -9,12 +9,14 @@
 //     (one vector = 16 B of 16-bit data or 2 x 16 B of fp32); all base
 //     indices are multiples of 8, so the vectors of all streams start at the
 //     same flat indices and only the ends of a range need scalar peels;
-//   * the fused step is a persistent multi-tensor kernel: each 64-lane
-//     wavefront walks the owner's chunk table with a grid stride and
-//     processes whole chunks (no cross-wave synchronisation at all);
+//   * one block per short contiguous piece: the fused step takes one chunk
+//     of the owner's chunk table per block, the flat-range kernels one piece
+//     of 256 (or 512) vectors, one vector per thread; blocks are dispatched
+//     in order, so the pieces in flight form a narrow window that advances
+//     through every stream (no cross-block synchronisation at all);
 //   * reductions of the squared norm use fp64 per-thread sums, a wavefront
-//     butterfly (DPP/permute shuffles), an LDS stage per block and a second
-//     single-block pass over the per-block partials -- a fixed tree, so the
+//     butterfly (DPP/permute shuffles), an LDS stage per block and fixed
+//     contiguous folds of the per-block partials -- a fixed tree, so the
 //     result is identical run to run;
 //   * the rank sum is one fp32 add per rank in rank order and one IEEE
 //     division (a multiply by 1/divisor when divisor is a power of two,
@@ -465,8 +467,8 @@ struct AdamArgs {
 //   RC == kReduced : a stored owner-local fp32 reduced gradient.
 constexpr int kReduced = -1;
 
-// Vectors per lane per iteration: two while the gradient loads of both fit in
-// about 64 VGPRs, else one.
+// Vectors per thread per iteration (chunks longer than one vector per thread):
+// two while the gradient loads of both fit in about 64 VGPRs, else one.
 template <int GDT, int RC>
 struct StepUnroll {
   static constexpr int loads = RC == kReduced ? 2 : RC * (GDT == ZERO_F32 ? 2 : 1);
