@@ -217,8 +217,9 @@ __device__ __forceinline__ void add_batch(const typename Elem<DT>::Raw (&x)[B][U
 
 // s += g_0 + ... + g_{R-1} (in rank order) for a runtime R, then divide.
 // Whole batches are double-buffered: batch b+1 is in flight while batch b is
-// added; the last R mod B ranks follow one at a time.
-template <int DT, int U>
+// added; the last R mod B ranks follow one at a time.  STREAM loads the rank
+// data with the nontemporal hint.
+template <int DT, int U, bool STREAM = false>
 __device__ __forceinline__ void reduce_vec(const RankSet& rs, const uint64_t (&f)[U],
                                            float (&s)[U][8]) {
   constexpr int B = RankBatch<DT>::value;
@@ -227,11 +228,11 @@ __device__ __forceinline__ void reduce_vec(const RankSet& rs, const uint64_t (&f
   uint32_t r0 = 0;
   if (full > 0) {
     Raw xa[B][U], xb[B][U];
-    load_batch<DT, U, B>(rs, 0, f, xa);
+    load_batch<DT, U, B, STREAM>(rs, 0, f, xa);
     for (; r0 + 2 * B <= full; r0 += 2 * B) {
-      load_batch<DT, U, B>(rs, r0 + B, f, xb);
+      load_batch<DT, U, B, STREAM>(rs, r0 + B, f, xb);
       add_batch<DT, U, B>(xa, s);
-      if (r0 + 2 * B < full) load_batch<DT, U, B>(rs, r0 + 2 * B, f, xa);
+      if (r0 + 2 * B < full) load_batch<DT, U, B, STREAM>(rs, r0 + 2 * B, f, xa);
       add_batch<DT, U, B>(xb, s);
     }
     if (r0 < full) {  // an odd number of whole batches: the last one is in xa
@@ -241,7 +242,7 @@ __device__ __forceinline__ void reduce_vec(const RankSet& rs, const uint64_t (&f
   }
   for (; r0 < rs.R; ++r0) {
     Raw x[1][U];
-    load_batch<DT, U, 1>(rs, r0, f, x);
+    load_batch<DT, U, 1, STREAM>(rs, r0, f, x);
     add_batch<DT, U, 1>(x, s);
   }
   divide_vec<U>(s, rs);
@@ -324,7 +325,7 @@ enum AccumMode : int {
 // so a block streams one short contiguous piece of each stream and exits, and
 // blocks are dispatched in order.  A grid smaller than the piece count (only
 // for ranges beyond kMaxChunkGrid pieces) takes the rest with a grid stride.
-template <int DT, int MODE, bool CHECK>
+template <int DT, int MODE, bool CHECK, bool STREAM>
 __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs a) {
   const uint64_t f0 = a.begin, f1 = a.end;
   const uint64_t a0 = min(f1, (f0 + 7) & ~7ull);
@@ -358,7 +359,7 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs a) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) s[0][k] = 0.0f;
       }
-      reduce_vec<DT, 1>(a.rs, f, s);
+      reduce_vec<DT, 1, STREAM>(a.rs, f, s);
       if (MODE == kAddMean) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) s[0][k] = old[k] + s[0][k];
@@ -672,10 +673,23 @@ void finish_check(const CheckOut& c, uint64_t parts, int32_t* d_overflow, double
                      d_sumsq, d_overflow);
 }
 
+template <int DT, int MODE, bool STREAM>
+void launch_reduce_s(const ReduceArgs& a, bool check, uint32_t grid, hipStream_t s) {
+  if (check) hipLaunchKernelGGL((reduce_kernel<DT, MODE, true, STREAM>), grid, kBlock, 0, s, a);
+  else hipLaunchKernelGGL((reduce_kernel<DT, MODE, false, STREAM>), grid, kBlock, 0, s, a);
+}
+
+// 16-bit rank data is loaded with the nontemporal hint below 32 ranks
+// (measured: +3% for one source, +6% for 16; -3% for 64 ranks).
 template <int DT, int MODE>
 void launch_reduce_m(const ReduceArgs& a, bool check, uint32_t grid, hipStream_t s) {
-  if (check) hipLaunchKernelGGL((reduce_kernel<DT, MODE, true>), grid, kBlock, 0, s, a);
-  else hipLaunchKernelGGL((reduce_kernel<DT, MODE, false>), grid, kBlock, 0, s, a);
+  if constexpr (DT != ZERO_F32) {
+    if (a.rs.R < 32) {
+      launch_reduce_s<DT, MODE, true>(a, check, grid, s);
+      return;
+    }
+  }
+  launch_reduce_s<DT, MODE, false>(a, check, grid, s);
 }
 
 template <int DT>
