@@ -25,7 +25,8 @@
  *     gives a message (thread-local, valid until the next call on the thread).
  *     No exceptions escape, nothing exits the process.
  *   - The caller owns every buffer.  The library allocates no memory and
- *     keeps no state between calls.  Arguments are validated before anything is
+ *     keeps no state between calls apart from a read-only cache of each
+ *     device's LDS sizes.  Arguments are validated before anything is
  *     launched; a call that fails validation launches nothing and writes
  *     nothing.  Buffer extents cannot be seen through plain pointers: the
  *     caller guarantees the sizes stated for each argument.

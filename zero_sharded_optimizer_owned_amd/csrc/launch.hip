@@ -18,6 +18,32 @@ int launch_status(const char* who) {
   return ZERO_OK;
 }
 
+namespace {
+constexpr int kMaxDevices = 64;
+int g_lds_cu[kMaxDevices];   // LDS bytes per CU, 0 = not yet queried
+int g_lds_blk[kMaxDevices];  // largest LDS allocation of one block
+}  // namespace
+
+uint32_t lds_for_blocks_per_cu(uint32_t per_cu) {
+  int dev = 0;
+  if (per_cu == 0 || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int cu = __atomic_load_n(&g_lds_cu[dev], __ATOMIC_ACQUIRE);
+  int blk = __atomic_load_n(&g_lds_blk[dev], __ATOMIC_RELAXED);
+  if (cu == 0) {
+    if (hipDeviceGetAttribute(&blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess ||
+        cu <= 0 || blk <= 0)
+      return 0;
+    __atomic_store_n(&g_lds_blk[dev], blk, __ATOMIC_RELAXED);
+    __atomic_store_n(&g_lds_cu[dev], cu, __ATOMIC_RELEASE);
+  }
+  // More than a (per_cu + 1)-th of the CU's LDS: per_cu blocks fit, one more does not.
+  const uint64_t bytes = ((uint64_t)cu / (per_cu + 1) + 1024 + 1023) / 1024 * 1024;
+  if (bytes * per_cu > (uint64_t)cu || bytes > (uint64_t)blk) return 0;
+  return (uint32_t)bytes;
+}
+
 uint32_t chunk_grid(uint64_t n_pieces, uint32_t requested) {
   if (requested) return requested;
   if (n_pieces == 0) return 1;

@@ -468,14 +468,6 @@ struct AdamArgs {
 //   RC == kReduced : a stored owner-local fp32 reduced gradient.
 constexpr int kReduced = -1;
 
-// Vectors per thread per iteration (chunks longer than one vector per thread):
-// two while the gradient loads of both fit in about 64 VGPRs, else one.
-template <int GDT, int RC>
-struct StepUnroll {
-  static constexpr int loads = RC == kReduced ? 2 : RC * (GDT == ZERO_F32 ? 2 : 1);
-  static constexpr int value = (RC != 0 && loads <= 8) ? 2 : 1;
-};
-
 template <int GDT, int PDT, int RC, int U>
 __device__ __forceinline__ void adam_vec(const AdamArgs& a, const uint64_t (&f)[U]) {
   float g[U][8], w[U][8], m[U][8], v[U][8];
@@ -547,7 +539,6 @@ __device__ __forceinline__ void adam_one(const AdamArgs& a, uint64_t f) {
 // the chunk count takes the remaining chunks with a grid stride.
 template <int GDT, int PDT, int RC>
 __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs a) {
-  constexpr int U = StepUnroll<GDT, RC>::value;
   const uint32_t t = threadIdx.x;
   for (uint64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
     const zero_chunk ch = a.chunks[c];
@@ -560,15 +551,8 @@ __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs a) {
     // boundary, threads 8-14 the tail after the last one.
     if (t < a0 - f0) adam_one<GDT, PDT, RC>(a, f0 + t);
     else if (t >= 8 && t - 8 < f1 - a1) adam_one<GDT, PDT, RC>(a, a1 + t - 8);
-    uint64_t vi = a0 / 8 + t;
     const uint64_t vend = a1 / 8;
-    if constexpr (U == 2) {
-      for (; vi + kBlock < vend; vi += 2 * kBlock) {
-        const uint64_t f[2] = {vi * 8, (vi + kBlock) * 8};
-        adam_vec<GDT, PDT, RC, 2>(a, f);
-      }
-    }
-    for (; vi < vend; vi += kBlock) {
+    for (uint64_t vi = a0 / 8 + t; vi < vend; vi += kBlock) {
       const uint64_t f[1] = {vi * 8};
       adam_vec<GDT, PDT, RC, 1>(a, f);
     }
@@ -699,9 +683,22 @@ void launch_reduce(const ReduceArgs& a, int mode, bool check, uint32_t grid, hip
   else launch_reduce_m<DT, kOverwrite>(a, check, grid, s);
 }
 
+// Blocks of the fused step resident on one CU.  Fewer blocks in flight keep
+// the window of pieces that HBM serves narrow; each block already has every
+// load of its vector in flight at once.  Measured on the 3.75e8-element owner
+// (one vector per thread, 2048-element chunks): two blocks per CU beat three,
+// four or an uncapped launch by 3-10% for 16-bit ranks, a stored gradient and
+// up to four fp32 ranks; from eight fp32 ranks on, one block per CU is 4-5%
+// faster than two.
+template <int GDT, int RC>
+uint32_t adam_blocks_per_cu(uint32_t R) {
+  return (GDT == ZERO_F32 && RC != kReduced && R >= 8) ? 1 : 2;
+}
+
 template <int GDT, int PDT, int RC>
 void launch_adam_k(const AdamArgs& a, uint32_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((adam_kernel<GDT, PDT, RC>), chunk_grid(a.n_chunks, grid), kBlock, 0, s, a);
+  hipLaunchKernelGGL((adam_kernel<GDT, PDT, RC>), chunk_grid(a.n_chunks, grid), kBlock,
+                     lds_for_blocks_per_cu(adam_blocks_per_cu<GDT, RC>(a.rs.R)), s, a);
 }
 
 template <int GDT, int RC>
