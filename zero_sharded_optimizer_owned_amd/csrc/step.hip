@@ -217,8 +217,8 @@ __device__ __forceinline__ void add_batch(const typename Elem<DT>::Raw (&x)[B][U
 
 // s += g_0 + ... + g_{R-1} (in rank order) for a runtime R, then divide.
 // Whole batches are double-buffered: batch b+1 is in flight while batch b is
-// added; the last R mod B ranks follow one at a time.  STREAM loads the rank
-// data with the nontemporal hint.
+// added; the loads of the last R mod B ranks are issued together before their
+// adds.  STREAM loads the rank data with the nontemporal hint.
 template <int DT, int U, bool STREAM = false>
 __device__ __forceinline__ void reduce_vec(const RankSet& rs, const uint64_t (&f)[U],
                                            float (&s)[U][8]) {
@@ -240,10 +240,27 @@ __device__ __forceinline__ void reduce_vec(const RankSet& rs, const uint64_t (&f
       r0 += B;
     }
   }
-  for (; r0 < rs.R; ++r0) {
-    Raw x[1][U];
-    load_batch<DT, U, 1, STREAM>(rs, r0, f, x);
-    add_batch<DT, U, 1>(x, s);
+  const uint32_t rem = rs.R - r0;  // < B, the same for every thread
+  if (rem > 0) {
+    Raw x[B - 1][U];
+#pragma unroll
+    for (int j = 0; j < B - 1; ++j) {
+      if ((uint32_t)j < rem) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          x[j][u] = STREAM ? Elem<DT>::load_stream(rs.ptr[r0 + j], f[u] - rs.base)
+                           : Elem<DT>::load_raw(rs.ptr[r0 + j], f[u] - rs.base);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < B - 1; ++j) {
+      if ((uint32_t)j < rem) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) s[u][k] = s[u][k] + Elem<DT>::widen(x[j][u], k);
+      }
+    }
   }
   divide_vec<U>(s, rs);
 }
