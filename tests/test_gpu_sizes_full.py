@@ -252,3 +252,41 @@ def test_per_backward_schedule_full_size():
     _check_coverage(w)
     del w
     torch.cuda.empty_cache()
+
+
+def test_flat_reduce_past_the_grid_cap():
+    """A flat range of more than 2^23 pieces (the launch's block cap): blocks take
+    the pieces past the grid with a grid stride, and the check folds 2^23
+    per-block partials in two stages.  One bf16 source and divisor 1, so each
+    output is the widened input; the inputs are dyadic, so the squared norm is
+    exact in fp64 whatever the summation order (closed form)."""
+    cap_elems = (1 << 23) * 2048
+    n = cap_elems + 12_345
+    c = 0.0625
+    g = torch.full((n,), c, dtype=torch.bfloat16, device="cuda")
+    special = {3: 0.5, cap_elems + 5: -0.25, n - 1: 0.125}
+    for i, x in special.items():
+        g[i] = x
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    ov = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ss = torch.zeros(1, dtype=torch.float64, device="cuda")
+    ws = zs.check_workspace(n, "cuda")
+    zs.zero_reduce_owned([g], 0, n, 1.0, out, check=(ov, ss, ws))
+    torch.cuda.synchronize()
+    want_sumsq = (n - len(special)) * c * c + sum(x * x for x in special.values())
+    assert int(ov.item()) == 0
+    assert ss.item() == want_sumsq
+    for i, x in special.items():
+        assert float(out[i]) == x
+    # every other element equals c: count them slice by slice on the device
+    step = 1 << 30
+    equal = 0
+    for lo in range(0, n, step):
+        equal += int(torch.count_nonzero(out[lo:lo + step] == c))
+    assert equal == n - len(special)
+    # a non-finite value in a piece past the grid cap sets the flag
+    g[cap_elems + 7] = float("inf")
+    zs.zero_reduce_owned([g], 0, n, 1.0, out, check=(ov, ss, ws))
+    assert int(ov.item()) == 1
+    del g, out, ws
+    torch.cuda.empty_cache()
