@@ -130,10 +130,11 @@ def step_stats(ms: list) -> dict | None:
 
 
 def ceilings(kname: str) -> dict:
-    """Measured ceilings for the dominant kernel: a plain copy and the probe
-    with the kernel's own read:write mix."""
+    """Measured ceilings for the dominant kernel: one stream read, one written,
+    a plain copy, and the probe with the kernel's own read:write mix."""
     n_src, n_dst = PROBE_MIX[kname]
-    return {"copy_gbps": round(probe_gbps(1, 1), 1), "mix": f"{n_src}:{n_dst}",
+    return {"read_gbps": round(probe_gbps(1, 0), 1), "write_gbps": round(probe_gbps(0, 1), 1),
+            "copy_gbps": round(probe_gbps(1, 1), 1), "mix": f"{n_src}:{n_dst}",
             "mix_gbps": round(probe_gbps(n_src, n_dst), 1), "kernel": "zero_stream_probe"}
 
 

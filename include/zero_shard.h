@@ -380,12 +380,14 @@ int zero_copy_spans(const zero_copy_span *spans, uint64_t n_spans, const void *c
  * zero_stream_probe -- the bandwidth probe against which the optimizer kernels
  * are measured (no part of the optimizer step; the pages define no such
  * operation).  Every destination receives the bytewise XOR of all sources:
- * dsts[d][i] = srcs[0][i] ^ ... ^ srcs[n_src-1][i] for i < bytes, streamed
- * with 16-byte loads and stores, one block per 256-vector piece, so one
- * launch moves (n_src + n_dst) * bytes bytes of HBM traffic.  With one source
- * and one destination it is a plain copy.
+ * dsts[d][i] = srcs[0][i] ^ ... ^ srcs[n_src-1][i] for i < bytes (all zero
+ * bytes without sources), streamed with 16-byte loads and stores, one block
+ * per 256-vector piece, so one launch moves (n_src + n_dst) * bytes bytes of
+ * HBM traffic.  One source and one destination is a plain copy; no
+ * destinations reads only, no sources writes only.
  * srcs[n_src], dsts[n_dst]  host arrays of device pointers, each 16-byte
- *                           aligned; 1 <= n_src, n_dst <= ZERO_MAX_PROBE_STREAMS
+ *                           aligned; n_src, n_dst <= ZERO_MAX_PROBE_STREAMS,
+ *                           not both 0 (an empty array may be NULL)
  * bytes                     bytes per stream, a multiple of 16 (0: no launch)
  * A destination that overlaps a source or another destination gives
  * unspecified contents (no fault: every access stays inside the streams).

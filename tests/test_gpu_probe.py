@@ -36,6 +36,22 @@ def test_probe_writes_xor_of_sources(n_src, n_dst, n_vec):
         assert np.all(got[4 * n_vec:].view(np.int32) == -7)  # nothing past the streams
 
 
+def test_probe_write_only_and_read_only():
+    n_vec = 64 * 256 + 3
+    dsts = [torch.full((4 * n_vec + 8,), -7, dtype=torch.int32, device="cuda") for _ in range(2)]
+    zs.zero_stream_probe([], [d[:4 * n_vec] for d in dsts])  # no sources: zeros
+    src = torch.arange(4 * n_vec, dtype=torch.int32, device="cuda")
+    keep = src.clone()
+    zs.zero_stream_probe([src], [])  # reads only
+    torch.cuda.synchronize()
+    for d in dsts:
+        got = d.cpu().numpy()
+        assert np.all(got[:4 * n_vec] == 0) and np.all(got[4 * n_vec:] == -7)
+    assert torch.equal(src, keep)
+    with pytest.raises(ValueError):
+        zs.zero_stream_probe([], [])
+
+
 def test_probe_rejects_mismatched_sizes():
     a = torch.zeros(64, dtype=torch.int32, device="cuda")
     b = torch.zeros(68, dtype=torch.int32, device="cuda")

@@ -419,12 +419,14 @@ def zero_stream_probe(srcs, dsts) -> None:
     """Bandwidth probe: every destination gets the bytewise XOR of all sources.
 
     All tensors are contiguous device tensors of one byte size (a multiple of
-    16); one launch moves (len(srcs) + len(dsts)) * that many bytes.
+    16); one launch moves (len(srcs) + len(dsts)) * that many bytes.  No
+    destinations: reads only; no sources: writes zeros.
     """
-    if not 1 <= len(srcs) <= ZERO_MAX_PROBE_STREAMS or not 1 <= len(dsts) <= ZERO_MAX_PROBE_STREAMS:
-        raise ValueError(f"between 1 and {ZERO_MAX_PROBE_STREAMS} sources and destinations")
-    nbytes = srcs[0].numel() * srcs[0].element_size()
-    sa, da = (ct.c_void_p * len(srcs))(), (ct.c_void_p * len(dsts))()
+    if len(srcs) > ZERO_MAX_PROBE_STREAMS or len(dsts) > ZERO_MAX_PROBE_STREAMS or not (srcs or dsts):
+        raise ValueError(f"at most {ZERO_MAX_PROBE_STREAMS} sources and destinations, not none of both")
+    first = (list(srcs) + list(dsts))[0]
+    nbytes = first.numel() * first.element_size()
+    sa, da = (ct.c_void_p * max(1, len(srcs)))(), (ct.c_void_p * max(1, len(dsts)))()
     for arr, ts, name in ((sa, srcs, "srcs"), (da, dsts, "dsts")):
         for i, t in enumerate(ts):
             _dev(t, f"{name}[{i}]")

@@ -23,7 +23,9 @@ constexpr int kProbeBatch = 4;  // sources whose loads are issued together
 // [b * kBlock, (b + 1) * kBlock) of every stream, blocks dispatched in order
 // (a grid smaller than the piece count takes the rest with a grid stride).
 // Loads of kProbeBatch sources are issued before they are combined; the XOR
-// is then stored to every destination.
+// is then stored to every destination.  Without destinations the XOR is only
+// kept live (an empty asm statement takes it as an operand), so the loads
+// stay and nothing is written.
 __global__ void __launch_bounds__(kBlock) probe_kernel(const ProbeArgs a) {
   const uint64_t stride = (uint64_t)gridDim.x * kBlock;
   for (uint64_t i = (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < a.n_vec; i += stride) {
@@ -42,6 +44,7 @@ __global__ void __launch_bounds__(kBlock) probe_kernel(const ProbeArgs a) {
         x.w ^= y[j].w;
       }
     }
+    asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
     for (uint32_t d = 0; d < a.n_dst; ++d) a.dst[d][i] = x;
   }
 }
@@ -55,13 +58,13 @@ extern "C" int zero_stream_probe(const void* const* srcs, uint32_t n_src, void* 
                                  uint32_t n_dst, uint64_t bytes, hipStream_t stream) {
   static const char* who = "zero_stream_probe";
   clear_error();
-  if (n_src < 1 || n_src > ZERO_MAX_PROBE_STREAMS || n_dst < 1 || n_dst > ZERO_MAX_PROBE_STREAMS)
-    return fail(ZERO_EINVAL, "%s: stream counts %u, %u outside [1, %d]", who, n_src, n_dst,
-                ZERO_MAX_PROBE_STREAMS);
+  if (n_src > ZERO_MAX_PROBE_STREAMS || n_dst > ZERO_MAX_PROBE_STREAMS || n_src + n_dst == 0)
+    return fail(ZERO_EINVAL, "%s: stream counts %u, %u: each at most %d, not both 0", who, n_src,
+                n_dst, ZERO_MAX_PROBE_STREAMS);
   if (bytes % 16) return fail(ZERO_EINVAL, "%s: %llu bytes is not a multiple of 16", who,
                               (unsigned long long)bytes);
   if (bytes == 0) return ZERO_OK;
-  if (!srcs || !dsts) return fail(ZERO_EINVAL, "%s: NULL pointer array", who);
+  if ((n_src && !srcs) || (n_dst && !dsts)) return fail(ZERO_EINVAL, "%s: NULL pointer array", who);
   ProbeArgs a{};
   for (uint32_t s = 0; s < n_src; ++s) {
     if (!srcs[s] || !aligned16(srcs[s]))
