@@ -720,7 +720,7 @@ def main():
                 "frac": round(achieved / PEAK_GBPS, 4),
                 "traffic": traffic_record(f"{kname}__{WORKLOAD_TAG[args.config]}"),
                 "kernel": kname, "kernel_ms": round(kernel_ms, 4),
-                "bytes_per_launch": w.kernel_bytes}
+                "bytes_per_launch": w.kernel_bytes, "bytes_per_param": round(w.kernel_bytes / n, 3)}
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "params/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
