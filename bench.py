@@ -296,6 +296,14 @@ class Workload:
         self.acc_owned = torch.empty(end - lb, dtype=torch.float32, device=self.dev)
         self.grads = [None]
 
+    def kernel_elements(self) -> int:
+        """Elements the dominant kernel processes per launch."""
+        if self.cfg == 5 and self.schedule == "accumulate":
+            return self.sh.padded_total
+        if self.cfg == 4 or self.schedule == "per-backward":
+            return self.sh.end - self.sh.begin
+        return self.sh.n_real
+
     def algorithmic_bytes(self) -> int:
         """Bytes the dominant kernel (the one that takes most of the step) moves per launch."""
         n = self.sh.n_real
@@ -720,7 +728,8 @@ def main():
                 "frac": round(achieved / PEAK_GBPS, 4),
                 "traffic": traffic_record(f"{kname}__{WORKLOAD_TAG[args.config]}"),
                 "kernel": kname, "kernel_ms": round(kernel_ms, 4),
-                "bytes_per_launch": w.kernel_bytes, "bytes_per_param": round(w.kernel_bytes / n, 3)}
+                "bytes_per_launch": w.kernel_bytes, "elements_per_launch": w.kernel_elements(),
+                "bytes_per_element": round(w.kernel_bytes / w.kernel_elements(), 3)}
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "params/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
