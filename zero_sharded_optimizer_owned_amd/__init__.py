@@ -172,6 +172,10 @@ def _dtype_code(t) -> int:
 def _dev(t, name: str, dtype=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if t.device.index != _torch().cuda.current_device():
+        # the kernels run on the current device's stream
+        raise ValueError(f"{name} lives on {t.device}, not on the current device "
+                         f"cuda:{_torch().cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
