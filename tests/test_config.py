@@ -42,6 +42,14 @@ def test_stage2_bf16_example_gives_four_data_ranks():
         step_config(_cfg("ds_config_stage2_bf16.json"), ranks=8)
 
 
+def test_bucket_bytes_follow_the_element_width():
+    """[Deep dive] "Let the engine own the microstep": the bucket size counts elements;
+    2e8 of them take 400 MB at two bytes and 800 MB at four."""
+    c = step_config(_cfg("ds_config_stage2_bf16.json"))
+    assert c["reduce_bucket_size"] * 2 == 400_000_000
+    assert c["reduce_bucket_size"] * 4 == 800_000_000
+
+
 def test_two_batch_fields_and_the_rank_count_fix_the_third():
     base = json.load(open(_cfg("ds_config_stage2_bf16.json")))
     for drop in ("train_batch_size", "train_micro_batch_size_per_gpu", "gradient_accumulation_steps"):

@@ -22,6 +22,15 @@ def test_printed_table_1p5e9_4_ranks():
         assert f"{float(sb[stage] / 2 ** 30):.2f}" == gib
 
 
+def test_printed_intro_and_seventy_b_totals():
+    """M1: 3 GB of two-byte weights inside 24 GB of state (21 GB more); M5: 1.12 TB for 70e9 in DP."""
+    for params, ranks, what, want in _rows("state_bytes_intro.txt"):
+        sb = oracle.state_bytes(int(params), int(ranks))
+        weights = int(params) * 2  # the estimator's two-byte compute weights
+        got = {"weights_2byte": weights, "DP": sb["DP"], "DP_minus_weights": sb["DP"] - weights}[what]
+        assert got == int(want)
+
+
 def test_printed_asserts():
     for p, r, pa, gr, op, stage, expected in _rows("state_bytes_asserts.txt"):
         sb = oracle.state_bytes(int(p), int(r), int(pa), int(gr), int(op))
