@@ -661,7 +661,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU exchange "
-              "around the owner step is not part of this build.", file=sys.stderr)
+              "around the owner step is not implemented here.", file=sys.stderr)
         sys.exit(2)
     import torch
 
