@@ -91,8 +91,10 @@ int zero_shard_layout(const uint64_t *numel, uint32_t n_tensors, uint32_t ranks,
                       uint32_t align_elems, uint64_t *tensor_offset, uint64_t *padded_total,
                       uint64_t *owner_begin, uint64_t *owner_end);
 
-/* One piece of an owner's work: `len` real elements from flat index `flat`, all
- * inside tensor `tensor`.  16 bytes; the device step reads an array of these. */
+/* One piece of an owner's work: `len` real elements from flat index `flat`.
+ * `tensor` holds the first of them; the piece may run on into the following
+ * tensors when no padding separates them.  16 bytes; the device calls read an
+ * array of these. */
 typedef struct {
   uint64_t flat;
   uint32_t len;
@@ -104,10 +106,12 @@ typedef struct {
  *
  * The real elements of [begin, end) are the union over tensors of
  * [tensor_offset[k], tensor_offset[k] + numel[k]) intersected with it (the
- * padding after each tensor is skipped).  Each intersection is cut at the
- * flat multiples of `max_chunk_elems`, so interior cuts fall on 128-bit
- * vector boundaries.  Chunks come out in increasing flat order and cover
- * every real element of the range exactly once.
+ * padding after each tensor is skipped).  Maximal runs of real elements --
+ * consecutive tensors with no padding between them count as one run, so many
+ * small tensors still make full-size chunks -- are cut at the flat multiples
+ * of `max_chunk_elems`, so interior cuts fall on 128-bit vector boundaries.
+ * Chunks come out in increasing flat order and cover every real element of
+ * the range exactly once.
  *
  * numel, tensor_offset [n_tensors] in: as from zero_shard_layout (offsets
  *                      increasing, tensors not overlapping)
@@ -286,9 +290,12 @@ int zero_adam_step(const zero_adam_args *args, hipStream_t stream);
  * trajectory than a full-state restore).  Calling zero_owner_to_dense for
  * every owner of a layout fills the whole dense buffer.
  *
- * For every real element f of the chunk table within [begin, end), in chunk
- * c = (flat, len, k):  dense[dense_offset[k] + f - tensor_offset[k]]  <->
- * owner[f - owner_base].
+ * For every real element f of the chunk table within [begin, end), with k the
+ * tensor that holds f:  dense[dense_offset[k] + f - tensor_offset[k]]  <->
+ * owner[f - owner_base].  (A chunk runs across tensors only where no padding
+ * separates them; there, with dense_offset as below, its first tensor gives
+ * the same dense index for every element, and that is how the kernel
+ * computes it.)
  * chunks[n_chunks]            device: the owner's chunk table
  * tensor_offset, dense_offset device uint64 [n_tensors]: flat and dense start of
  *                             each tensor (dense_offset[k] = sum of numel[j<k])

@@ -80,12 +80,28 @@ def test_chunk_table_covers_real_elements_exactly_once():
             want = oracle.real_ranges(numels, list(off), int(b[r]), int(e[r]))
             elems = [f for s, t in got for f in range(s, t)]
             assert elems == [f for s, t in want for f in range(s, t)]
-            for c in ch:
+            for i, c in enumerate(ch):
                 k = int(c["tensor"])
-                assert off[k] <= c["flat"] and c["flat"] + c["len"] <= off[k] + numels[k]
+                assert off[k] <= c["flat"] < off[k] + numels[k]  # the tensor of its first element
                 assert 1 <= c["len"] <= C
-                # a chunk never crosses a multiple of C
+                # a chunk never crosses a multiple of C ...
                 assert int(c["flat"]) // C == (int(c["flat"]) + int(c["len"]) - 1) // C
+                # ... and is cut nowhere else: flat-contiguous neighbours meet at a multiple of C
+                if i > 0 and int(ch[i - 1]["flat"]) + int(ch[i - 1]["len"]) == int(c["flat"]):
+                    assert int(c["flat"]) % C == 0
+
+
+def test_chunk_table_merges_tensors_without_padding():
+    """Many small tensors whose sizes are multiples of the alignment have no
+    padding between them, so they share full-size chunks."""
+    numels = [64] * 1000 + [100] + [64] * 10
+    off, total, b, e = zs.zero_shard_layout(numels, 1, 64)
+    ch = zs.zero_chunk_table(numels, off, int(b[0]), int(e[0]), 2048)
+    lens = [int(x) for x in ch["len"]]
+    # 64,000 contiguous elements = 31 full chunks + 512, then 100 + 28 padding, then 640 more
+    assert lens[:31] == [2048] * 31 and lens[31] == 512 + 100
+    assert lens[32:] == [640]
+    assert [int(x) for x in ch["tensor"][:3]] == [0, 32, 64]
 
 
 def test_chunk_table_capacity_and_errors():

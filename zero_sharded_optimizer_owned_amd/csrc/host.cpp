@@ -89,21 +89,27 @@ extern "C" int zero_chunk_table(const uint64_t* numel, const uint64_t* tensor_of
   }
   const uint64_t C = max_chunk_elems;
   uint64_t count = 0;
-  for (uint32_t k = 0; k < n_tensors; ++k) {
-    const uint64_t t0 = tensor_offset[k], t1 = tensor_offset[k] + numel[k];
-    uint64_t b = t0 > begin ? t0 : begin;
-    const uint64_t e = t1 < end ? t1 : end;
+  for (uint32_t k = 0; k < n_tensors;) {
+    // a run of tensors k .. j-1 with no padding between them
+    uint32_t j = k + 1;
+    while (j < n_tensors && tensor_offset[j] == tensor_offset[j - 1] + numel[j - 1]) ++j;
+    const uint64_t r0 = tensor_offset[k], r1 = tensor_offset[j - 1] + numel[j - 1];
+    uint64_t b = r0 > begin ? r0 : begin;
+    const uint64_t e = r1 < end ? r1 : end;
+    uint32_t t = k;  // the tensor that holds flat index b
     while (b < e) {
+      while (tensor_offset[t] + numel[t] <= b) ++t;
       const uint64_t cut = (b / C + 1) * C;  // next multiple of C after b
       const uint64_t stop = cut < e ? cut : e;
       if (out && count < capacity) {
         out[count].flat = b;
         out[count].len = (uint32_t)(stop - b);
-        out[count].tensor = k;
+        out[count].tensor = t;
       }
       ++count;
       b = stop;
     }
+    k = j;
   }
   *n_chunks = count;
   if (out == nullptr && capacity == 0) return ZERO_OK;
