@@ -224,12 +224,39 @@ int zero_grad_check(const float *g, uint64_t n, int32_t *d_overflow, double *d_s
  * -------------------------------------------------------------------------- */
 int zero_clip_coef(double sumsq, double max_norm, double eps, float *coef);
 
+/* ----------------------------------------------------------------------------
+ * zero_chunk_groups -- packs runs of short chunks into groups that one block
+ * of zero_adam_step processes together (host only; a layout aid, not a step
+ * of the method).  Walking the chunks in order, a group is either one chunk,
+ * or consecutive chunks whose work units -- scalar head elements, 128-bit
+ * vectors and scalar tail elements -- number at most 256 in all and whose
+ * elements number at most max_group_elems.  Tensors whose padding breaks the
+ * runs of real elements (e.g. 100-element tensors padded to 128) otherwise
+ * give one almost idle block each.
+ *
+ * chunks[n_chunks]     in : a host copy of the chunk table
+ * max_group_elems      in : > 0 (the chunk size is the natural choice)
+ * out[capacity]        out: the first chunk of each group, then n_chunks as a
+ *                      sentinel (n_groups + 1 entries); out == NULL with
+ *                      capacity == 0 only counts
+ * n_groups             out: number of groups, also on ERANGE
+ * Errors: EINVAL (NULL pointers, max_group_elems 0); ERANGE (capacity below
+ * n_groups + 1).
+ * -------------------------------------------------------------------------- */
+int zero_chunk_groups(const zero_chunk *chunks, uint64_t n_chunks, uint32_t max_group_elems,
+                      uint64_t *out, uint64_t capacity, uint64_t *n_groups);
+
 /* Arguments of zero_adam_step. */
 typedef struct {
   /* The owner's work: device chunk table (from zero_chunk_table) and the owner
    * range [begin, end); chunk pieces outside the range are ignored. */
   const zero_chunk *chunks;
   uint64_t n_chunks;
+  /* Optional device group table from zero_chunk_groups (n_groups + 1 entries):
+   * one block per group instead of one per chunk.  NULL (and n_groups 0): one
+   * block per chunk.  The results are the same either way. */
+  const uint64_t *groups;
+  uint64_t n_groups;
   uint64_t begin, end;
   /* Gradient source: either R rank buffers (reduced here, as zero_reduce_owned,
    * then multiplied by clip_coef) or, with reduced_g != NULL, an owner-local
@@ -253,9 +280,10 @@ typedef struct {
   int32_t adamw; /* 1: decoupled decay (AdamW); 0: classic Adam, wd added to g */
   uint64_t step;
   double clip_coef; /* 1.0 when not clipping */
-  uint32_t grid_blocks; /* 0: one block per chunk (the library default); else
-                           that many blocks, each taking chunks with a grid
-                           stride (same results for every grid) */
+  uint32_t grid_blocks; /* 0: one block per chunk or group (the library
+                           default); else that many blocks, each taking chunks
+                           or groups with a grid stride (same results for
+                           every grid) */
 } zero_adam_args;
 
 /* ----------------------------------------------------------------------------

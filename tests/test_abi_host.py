@@ -270,3 +270,41 @@ def test_stage3_span_tables_reproduce_the_oracle():
         assert all(int(s["len"]) >= 1 for s in spans)
         _apply_spans(spans, shards, got)
         assert np.array_equal(got, want)
+
+
+def _units(flat, ln):
+    a0 = min(flat + ln, (flat + 7) // 8 * 8)
+    a1 = max(a0, (flat + ln) // 8 * 8)
+    return (a0 - flat) + (a1 - a0) // 8 + (flat + ln - a1)
+
+
+def test_chunk_groups_partition_the_table():
+    """Groups cover the chunks in order; a group of several chunks holds at most
+    256 work units and at most max_group elements; greedy, so no group could
+    have taken its successor's first chunk."""
+    rnd = random.Random(11)
+    for _ in range(200):
+        numels = [rnd.randrange(1, rnd.choice([20, 200, 5000])) for _ in range(rnd.randrange(1, 60))]
+        A = rnd.choice([1, 8, 64])
+        off, total, b, e = zs.zero_shard_layout(numels, 1, A)
+        C = rnd.choice([64, 512, 2048])
+        ch = zs.zero_chunk_table(numels, off, int(b[0]), int(e[0]), C)
+        g = zs.zero_chunk_groups(ch, C)
+        assert g[0] == 0 and g[-1] == ch.size and np.all(np.diff(g.astype(np.int64)) > 0)
+        for i in range(g.size - 1):
+            part = ch[int(g[i]):int(g[i + 1])]
+            u = sum(_units(int(c["flat"]), int(c["len"])) for c in part)
+            if part.size > 1:
+                assert u <= 256 and int(part["len"].sum()) <= C
+            if i + 2 < g.size and _units(int(part[0]["flat"]), int(part[0]["len"])) <= 256:
+                nxt = ch[int(g[i + 1])]
+                grown_u = u + _units(int(nxt["flat"]), int(nxt["len"]))
+                assert grown_u > 256 or int(part["len"].sum()) + int(nxt["len"]) > C
+    L = zs.lib()
+    ch = zs.zero_chunk_table([10] * 8, zs.zero_shard_layout([10] * 8, 1, 16)[0], 0, 128, 64)
+    cnt = np.zeros(1, dtype=np.uint64)
+    out = np.zeros(1, dtype=np.uint64)
+    assert L.zero_chunk_groups(ch.ctypes.data, ch.size, 64, out.ctypes.data, 1, cnt.ctypes.data) == zs.ZERO_ERANGE
+    assert int(cnt[0]) == 2  # 8 chunks of 10 elements (3 units each): 6 + 2 under the 64-element bound
+    assert L.zero_chunk_groups(ch.ctypes.data, ch.size, 0, None, 0, cnt.ctypes.data) == zs.ZERO_EINVAL
+    assert L.zero_chunk_groups(None, 3, 64, None, 0, cnt.ctypes.data) == zs.ZERO_EINVAL

@@ -190,6 +190,8 @@ LAYOUTS = {
     "tiny_tensors": ([1, 2, 3, 5, 7, 8, 9, 15, 16, 17, 31, 33, 63, 64, 65, 100] * 6, 5, 8),
     "empty_owners": ([3, 2], 9, 1),
     "one_big": ([123_457], 4, 64),
+    # padding after almost every tensor: short chunks that the group table packs
+    "padded_tiny": ([1 + (37 * k) % 150 for k in range(300)], 3, 64),
 }
 
 
@@ -208,12 +210,17 @@ def _owner_inputs(numels, R, A, owner, gcode, seed):
 @pytest.mark.parametrize("layout", list(LAYOUTS))
 @pytest.mark.parametrize("gcode,pcode", [(F16, F16), (BF16, BF16), (F32, BF16), (F32, 0), (F16, BF16)])
 @pytest.mark.parametrize("max_chunk", [64, 2048])
-def test_adam_step_matches_oracle(layout, gcode, pcode, max_chunk):
+@pytest.mark.parametrize("grouped", [False, True])
+def test_adam_step_matches_oracle(layout, gcode, pcode, max_chunk, grouped):
     numels, R, A = LAYOUTS[layout]
     for owner in range(R):
         off, total, begin, end, lb, grads, w, m, v = _owner_inputs(numels, R, A, owner, gcode, owner + 1)
         chunks = zs.zero_chunk_table(numels, off, begin, end, max_chunk)
         dchunks = zs.chunks_to_device(chunks) if chunks.size else None
+        gkw = {}
+        if grouped and chunks.size:
+            groups = zs.zero_chunk_groups(chunks, max_chunk)
+            gkw = dict(groups_dev=torch.from_numpy(groups.astype(np.int64)).to(DEV), n_groups=groups.size - 1)
         dgr = [to_dev(g, gcode) for g in grads]
         dw, dm, dv = to_dev(w, F32), to_dev(m, F32), to_dev(v, F32)
         sentinel = 0x7BFF if pcode == F16 else 0x3F80
@@ -224,7 +231,7 @@ def test_adam_step_matches_oracle(layout, gcode, pcode, max_chunk):
         for t in (11, 12, 13):  # independent trajectories, three steps
             zs.zero_adam_step(chunks_dev=dchunks, n_chunks=chunks.size, begin=begin, end=end,
                               master=dw, exp_avg=dm, exp_avg_sq=dv, local_base=lb, step=t,
-                              rank_grads=dgr, divisor=float(R), param16=dp, **HP)
+                              rank_grads=dgr, divisor=float(R), param16=dp, **gkw, **HP)
             oracle.owner_step(ranges, oracle.hyper(step=t, **HP), ow, om, ov_, lb, grads=grads,
                               gdtype=gcode, divisor=float(R), p16=p16_host if pcode else None,
                               pdtype=pcode)
@@ -239,6 +246,42 @@ def test_adam_step_matches_oracle(layout, gcode, pcode, max_chunk):
                     real[s:e_] = True
                 assert np.all(got[~real] == sentinel), what + ": padding or foreign elements written"
                 assert_p16_within_ulp(got[real], p16_host[real], what + " p16")
+
+
+def test_group_tables_give_the_same_bits():
+    """One block per chunk, the packed group table, a hand-made group of 300
+    chunks (more chunks and more work units than one block has threads) and a
+    small grid that strides over the groups: identical bits every way."""
+    numels, R, A = [1 + (53 * k) % 120 for k in range(700)], 2, 64
+    off, total, b, e = zs.zero_shard_layout(numels, R, A)
+    begin, end = int(b[1]), int(e[1])
+    lb = begin & ~7
+    grads = [to_dev(g, F16) for g in _rank_inputs(F16, R, total, seed=12)]
+    w0 = gen(12, synth.STREAM_MASTER, end - lb, synth.DIST_NORMAL, 0.02, F32)
+    chunks = zs.zero_chunk_table(numels, off, begin, end, 2048)
+    dch = zs.chunks_to_device(chunks)
+    packed = zs.zero_chunk_groups(chunks, 2048)
+    assert packed.size - 1 < chunks.size // 4
+    n = chunks.size
+    handmade = np.array([0, 1, 301] + ([n] if n > 301 else []), dtype=np.uint64)
+    handmade = np.unique(np.minimum(handmade, n))
+    variants = [dict(), dict(groups=packed), dict(groups=handmade), dict(groups=packed, grid_blocks=3)]
+    results = []
+    for v in variants:
+        dw = to_dev(w0, F32)
+        dm, dv = torch.zeros_like(dw), torch.zeros_like(dw)
+        p16 = torch.zeros(total, dtype=torch.float16, device=DEV)
+        kw = {}
+        if "groups" in v:
+            g = v["groups"]
+            kw = dict(groups_dev=torch.from_numpy(g.astype(np.int64)).to(DEV), n_groups=g.size - 1)
+        zs.zero_adam_step(chunks_dev=dch, n_chunks=n, begin=begin, end=end, master=dw, exp_avg=dm, exp_avg_sq=dv,
+                          local_base=lb, step=2, rank_grads=grads, divisor=2.0, param16=p16,
+                          grid_blocks=v.get("grid_blocks", 0), **kw, **HP)
+        results.append([from_dev(x).view(np.uint32) for x in (dw, dm, dv)] + [from_dev(p16)])
+    for r in results[1:]:
+        for x, y in zip(r, results[0]):
+            assert np.array_equal(x, y)
 
 
 @pytest.mark.parametrize("adamw,wd", [(False, 0.05), (False, 0.0), (True, 0.01)])

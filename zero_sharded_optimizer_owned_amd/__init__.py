@@ -31,7 +31,7 @@ EXPORTED = ("zero_last_error", "zero_shard_layout", "zero_chunk_table", "zero_st
             "zero_reduce_owned", "zero_grad_check", "zero_clip_coef", "zero_adam_step",
             "zero_owner_to_dense", "zero_dense_to_owner", "zero3_storage", "zero3_gather_spans",
             "zero3_partition_spans", "zero_copy_spans", "zero_stream_probe",
-            "zero_check_workspace_bytes")
+            "zero_check_workspace_bytes", "zero_chunk_groups")
 
 CHUNK_DTYPE = np.dtype([("flat", "<u8"), ("len", "<u4"), ("tensor", "<u4")])
 SPAN_DTYPE = np.dtype([("src", "<u8"), ("dst", "<u8"), ("len", "<u4"), ("buf", "<u4")])
@@ -47,7 +47,8 @@ class ZeroShardError(RuntimeError):
 
 class AdamArgs(ct.Structure):
     _fields_ = [
-        ("chunks", ct.c_void_p), ("n_chunks", ct.c_uint64), ("begin", ct.c_uint64),
+        ("chunks", ct.c_void_p), ("n_chunks", ct.c_uint64), ("groups", ct.c_void_p),
+        ("n_groups", ct.c_uint64), ("begin", ct.c_uint64),
         ("end", ct.c_uint64),
         ("rank_grads", ct.c_void_p), ("R", ct.c_uint32), ("grad_dtype", ct.c_int32),
         ("grad_base", ct.c_uint64), ("divisor", ct.c_float), ("reduced_g", ct.c_void_p),
@@ -90,6 +91,7 @@ def load(path: str):
     L.zero_copy_spans.argtypes = [P, U64, P, P, U32, P, U64, U32, P]
     L.zero_stream_probe.argtypes = [P, U32, P, U32, U64, P]
     L.zero_check_workspace_bytes.argtypes = [U64, P]
+    L.zero_chunk_groups.argtypes = [P, U64, U32, P, U64, P]
     return L
 
 
@@ -140,6 +142,17 @@ def zero_chunk_table(numels: Sequence[int], offsets: Sequence[int], begin: int, 
     out = np.zeros(int(count[0]), dtype=CHUNK_DTYPE)
     _check(lib().zero_chunk_table(_p(n), _p(off), n.size, begin, end, max_chunk,
                                   _p(out) if out.size else None, out.size, _p(count)))
+    return out
+
+
+def zero_chunk_groups(chunks: np.ndarray, max_group: int) -> np.ndarray:
+    """Group table (first chunk of each group, then len(chunks)) packing runs of
+    short chunks for zero_adam_step; uint64, n_groups + 1 entries."""
+    ch = np.ascontiguousarray(chunks, dtype=CHUNK_DTYPE)
+    count = np.zeros(1, dtype=np.uint64)
+    _check(lib().zero_chunk_groups(_p(ch), ch.size, max_group, None, 0, _p(count)))
+    out = np.zeros(int(count[0]) + 1, dtype=np.uint64)
+    _check(lib().zero_chunk_groups(_p(ch), ch.size, max_group, _p(out), out.size, _p(count)))
     return out
 
 
@@ -273,8 +286,9 @@ def zero_adam_step(*, chunks_dev, n_chunks: int, begin: int, end: int, master, e
                    local_base: int, step: int, lr: float, beta1: float, beta2: float, eps: float,
                    weight_decay: float = 0.0, adamw: bool = True, rank_grads=None, grad_base: int = 0,
                    divisor: float = 1.0, reduced_g=None, param16=None, param_base: int = 0,
-                   clip_coef: float = 1.0, grid_blocks: int = 0) -> None:
-    """Fused reduce + Adam/AdamW + 16-bit write-back over a device chunk table.
+                   clip_coef: float = 1.0, grid_blocks: int = 0, groups_dev=None, n_groups: int = 0) -> None:
+    """Fused reduce + Adam/AdamW + 16-bit write-back over a device chunk table
+    (optionally packed by a device group table from ``zero_chunk_groups``).
 
     The kernel touches only flat indices in [begin, end) (chunk pieces outside are
     ignored), so every buffer is checked to hold those.
@@ -291,6 +305,13 @@ def zero_adam_step(*, chunks_dev, n_chunks: int, begin: int, end: int, master, e
     a = AdamArgs()
     a.chunks = chunks_dev.data_ptr() if chunks_dev is not None else None
     a.n_chunks, a.begin, a.end = n_chunks, begin, end
+    if groups_dev is not None:
+        _dev(groups_dev, "groups", torch.int64)
+        if groups_dev.numel() < n_groups + 1:
+            raise ValueError("group table smaller than n_groups + 1")
+        a.groups, a.n_groups = groups_dev.data_ptr(), n_groups
+    elif n_groups:
+        raise ValueError("n_groups given without a group table")
     keep = None
     if reduced_g is not None:
         _dev(reduced_g, "reduced_g", torch.float32)
@@ -461,6 +482,12 @@ class OwnerShard:
         self.chunks = zero_chunk_table(self.numels, self.offsets, self.begin, self.end, max_chunk)
         self.device = torch.device(device or "cuda")
         self.chunks_dev = chunks_to_device(self.chunks, self.device)
+        # short chunks packed several to a block, when that saves blocks
+        self.groups = zero_chunk_groups(self.chunks, max_chunk)
+        self.n_groups = self.groups.size - 1
+        self.groups_dev = None
+        if self.n_groups < self.chunks.size:
+            self.groups_dev = torch.from_numpy(self.groups.astype(np.int64)).to(self.device)
         self.n_real = int(self.chunks["len"].sum()) if self.chunks.size else 0
         self.align = align
         self.dense_total = int(sum(self.numels))
@@ -482,6 +509,7 @@ class OwnerShard:
                        exp_avg_sq=self.exp_avg_sq, local_base=self.local_base, step=step,
                        rank_grads=rank_grads, grad_base=grad_base, divisor=divisor,
                        reduced_g=reduced_g, param16=param16, param_base=param_base,
+                       groups_dev=self.groups_dev, n_groups=self.n_groups if self.groups_dev is not None else 0,
                        clip_coef=clip_coef, grid_blocks=grid_blocks, **hyper)
 
     # -- export / import of fp32 shard data in the dense per-tensor layout

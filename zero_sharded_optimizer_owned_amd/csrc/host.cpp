@@ -119,6 +119,48 @@ extern "C" int zero_chunk_table(const uint64_t* numel, const uint64_t* tensor_of
   return ZERO_OK;
 }
 
+extern "C" int zero_chunk_groups(const zero_chunk* chunks, uint64_t n_chunks, uint32_t max_group_elems,
+                                 uint64_t* out, uint64_t capacity, uint64_t* n_groups) {
+  zs::clear_error();
+  if (!n_groups) return fail(ZERO_EINVAL, "zero_chunk_groups: n_groups is NULL");
+  if (n_chunks > 0 && !chunks) return fail(ZERO_EINVAL, "zero_chunk_groups: chunks is NULL");
+  if (max_group_elems == 0) return fail(ZERO_EINVAL, "zero_chunk_groups: max_group_elems must be > 0");
+  if (capacity > 0 && !out) return fail(ZERO_EINVAL, "zero_chunk_groups: out is NULL");
+  // work units of a chunk: scalar head, 128-bit vectors, scalar tail
+  auto units = [](const zero_chunk& c) -> uint64_t {
+    const uint64_t f0 = c.flat, f1 = c.flat + c.len;
+    uint64_t a0 = (f0 + 7) & ~7ull;
+    if (a0 > f1) a0 = f1;
+    uint64_t a1 = f1 & ~7ull;
+    if (a1 < a0) a1 = a0;
+    return (a0 - f0) + (a1 - a0) / 8 + (f1 - a1);
+  };
+  const uint64_t kUnits = 256;  // one unit per thread of a 256-thread block
+  uint64_t g = 0;
+  for (uint64_t i = 0; i < n_chunks;) {
+    if (out && g < capacity) out[g] = i;
+    ++g;
+    uint64_t u = units(chunks[i]), elems = chunks[i].len, j = i + 1;
+    if (u <= kUnits) {
+      while (j < n_chunks) {
+        const uint64_t uj = units(chunks[j]);
+        if (u + uj > kUnits || elems + chunks[j].len > max_group_elems) break;
+        u += uj;
+        elems += chunks[j].len;
+        ++j;
+      }
+    }
+    i = j;
+  }
+  if (out && g < capacity) out[g] = n_chunks;  // sentinel
+  *n_groups = g;
+  if (out == nullptr && capacity == 0) return ZERO_OK;
+  if (g + 1 > capacity)
+    return fail(ZERO_ERANGE, "zero_chunk_groups: %llu entries needed, capacity %llu",
+                (unsigned long long)(g + 1), (unsigned long long)capacity);
+  return ZERO_OK;
+}
+
 namespace {
 // whole + shared / R as a reduced fraction; whole and shared are exact
 // products of 64-bit by 32-bit values (at most 2^98), R < 2^64.

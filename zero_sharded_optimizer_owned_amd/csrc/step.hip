@@ -470,6 +470,8 @@ struct AdamArgs {
   RankSet rs;
   const zero_chunk* chunks;
   uint64_t n_chunks;
+  const uint64_t* groups;  // [n_groups + 1] first chunk of each block's work, or NULL
+  uint64_t n_groups;
   uint64_t begin, end;
   const float* reduced_g;
   float *w, *m, *v;
@@ -548,31 +550,107 @@ __device__ __forceinline__ void adam_one(const AdamArgs& a, uint64_t f) {
   if constexpr (PDT != ZERO_NONE) Elem<PDT>::store1(a.p16, f - a.param_base, w);
 }
 
-// Multi-tensor kernel, one block per chunk: the block's threads take the
-// chunk's 128-bit vectors in order (thread t on vectors t, t + kBlock, ...),
-// so a block streams one short contiguous piece of every stream and exits.
-// Blocks are dispatched in chunk order, which keeps the pieces in flight
-// across the chip inside a narrow window of each stream.  A grid smaller than
-// the chunk count takes the remaining chunks with a grid stride.
+// One chunk by one block: the block's threads take the chunk's 128-bit
+// vectors in order (thread t on vectors t, t + kBlock, ...); threads 0-6 take
+// the scalar head before the first vector boundary, threads 8-14 the tail
+// after the last one.
+template <int GDT, int PDT, int RC>
+__device__ __forceinline__ void adam_chunk(const AdamArgs& a, const zero_chunk ch, uint32_t t) {
+  const uint64_t f0 = max(ch.flat, a.begin);
+  const uint64_t f1 = min(ch.flat + ch.len, a.end);
+  if (f0 >= f1) return;
+  const uint64_t a0 = min(f1, (f0 + 7) & ~7ull);
+  const uint64_t a1 = max(a0, f1 & ~7ull);
+  if (t < a0 - f0) adam_one<GDT, PDT, RC>(a, f0 + t);
+  else if (t >= 8 && t - 8 < f1 - a1) adam_one<GDT, PDT, RC>(a, a1 + t - 8);
+  const uint64_t vend = a1 / 8;
+  for (uint64_t vi = a0 / 8 + t; vi < vend; vi += kBlock) {
+    const uint64_t f[1] = {vi * 8};
+    adam_vec<GDT, PDT, RC, 1>(a, f);
+  }
+}
+
+// Several short chunks by one block.  Each chunk is cut into work units --
+// its scalar head elements, its 128-bit vectors and its scalar tail elements
+// -- and the block's threads take the units of all its chunks together
+// (thread t on units t, t + kBlock, ...), finding a unit's chunk by binary
+// search over the prefix sums of the unit counts.  The units run the same
+// element and vector routines as above, so the results are identical to one
+// block per chunk.  Chunks are taken kBlock at a time.
+template <int GDT, int PDT, int RC>
+__device__ void adam_packed(const AdamArgs& a, uint64_t c0, uint64_t c1, uint32_t t) {
+  __shared__ uint64_t s_f0[kBlock];
+  __shared__ uint32_t s_head[kBlock], s_nvec[kBlock];
+  __shared__ uint32_t s_pre[kBlock + 1];
+  for (uint64_t s0 = c0; s0 < c1; s0 += kBlock) {
+    const uint32_t m = (uint32_t)min((uint64_t)kBlock, c1 - s0);
+    uint32_t units = 0;
+    if (t < m) {
+      const zero_chunk ch = a.chunks[s0 + t];
+      const uint64_t f0 = max(ch.flat, a.begin);
+      const uint64_t f1 = max(f0, min(ch.flat + ch.len, a.end));
+      const uint64_t a0 = min(f1, (f0 + 7) & ~7ull);
+      const uint64_t a1 = max(a0, f1 & ~7ull);
+      s_f0[t] = f0;
+      s_head[t] = (uint32_t)(a0 - f0);
+      s_nvec[t] = (uint32_t)((a1 - a0) / 8);
+      units = (uint32_t)(a0 - f0) + (uint32_t)((a1 - a0) / 8) + (uint32_t)(f1 - a1);
+    }
+    // inclusive scan of the unit counts (Hillis-Steele over the block)
+    s_pre[t + 1] = units;
+    if (t == 0) s_pre[0] = 0;
+    __syncthreads();
+    for (uint32_t d = 1; d < kBlock; d <<= 1) {
+      const uint32_t x = t + 1 > d ? s_pre[t + 1 - d] : 0u;
+      __syncthreads();
+      s_pre[t + 1] += x;
+      __syncthreads();
+    }
+    const uint32_t total = s_pre[m];
+    for (uint32_t u = t; u < total; u += kBlock) {
+      uint32_t lo = 0, hi = m;  // the chunk j with s_pre[j] <= u < s_pre[j + 1]
+      while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) / 2;
+        if (s_pre[mid] <= u) lo = mid;
+        else hi = mid;
+      }
+      const uint32_t r = u - s_pre[lo];
+      const uint64_t f0 = s_f0[lo];
+      const uint32_t head = s_head[lo], nvec = s_nvec[lo];
+      if (r < head) {
+        adam_one<GDT, PDT, RC>(a, f0 + r);
+      } else if (r < head + nvec) {
+        const uint64_t f[1] = {f0 + head + 8ull * (r - head)};
+        adam_vec<GDT, PDT, RC, 1>(a, f);
+      } else {
+        adam_one<GDT, PDT, RC>(a, f0 + head + 8ull * nvec + (r - head - nvec));
+      }
+    }
+    __syncthreads();  // the next slice reuses the arrays
+  }
+}
+
+// Multi-tensor kernel, one block per piece of work: a chunk, or -- with a
+// group table -- a group of consecutive chunks (one long chunk, or several
+// short ones packed together).  A block streams one short contiguous piece
+// of every stream and exits; blocks are dispatched in order, which keeps the
+// pieces in flight across the chip inside a narrow window of each stream.  A
+// grid smaller than the piece count takes the remaining pieces with a grid
+// stride.
 template <int GDT, int PDT, int RC>
 __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs a) {
   const uint32_t t = threadIdx.x;
-  for (uint64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
-    const zero_chunk ch = a.chunks[c];
-    const uint64_t f0 = max(ch.flat, a.begin);
-    const uint64_t f1 = min(ch.flat + ch.len, a.end);
-    if (f0 >= f1) continue;
-    const uint64_t a0 = min(f1, (f0 + 7) & ~7ull);
-    const uint64_t a1 = max(a0, f1 & ~7ull);
-    // Scalar peels: threads 0-6 take the head before the first vector
-    // boundary, threads 8-14 the tail after the last one.
-    if (t < a0 - f0) adam_one<GDT, PDT, RC>(a, f0 + t);
-    else if (t >= 8 && t - 8 < f1 - a1) adam_one<GDT, PDT, RC>(a, a1 + t - 8);
-    const uint64_t vend = a1 / 8;
-    for (uint64_t vi = a0 / 8 + t; vi < vend; vi += kBlock) {
-      const uint64_t f[1] = {vi * 8};
-      adam_vec<GDT, PDT, RC, 1>(a, f);
+  const uint64_t n_work = a.groups ? a.n_groups : a.n_chunks;
+  for (uint64_t w = blockIdx.x; w < n_work; w += gridDim.x) {
+    if (!a.groups) {
+      adam_chunk<GDT, PDT, RC>(a, a.chunks[w], t);
+      continue;
     }
+    const uint64_t c0 = a.groups[w];
+    const uint64_t c1 = min(a.groups[w + 1], a.n_chunks);
+    if (c1 <= c0) continue;
+    if (c1 - c0 == 1) adam_chunk<GDT, PDT, RC>(a, a.chunks[c0], t);
+    else adam_packed<GDT, PDT, RC>(a, c0, c1, t);
   }
 }
 
@@ -714,7 +792,8 @@ uint32_t adam_blocks_per_cu(uint32_t R) {
 
 template <int GDT, int PDT, int RC>
 void launch_adam_k(const AdamArgs& a, uint32_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((adam_kernel<GDT, PDT, RC>), chunk_grid(a.n_chunks, grid), kBlock,
+  hipLaunchKernelGGL((adam_kernel<GDT, PDT, RC>),
+                     chunk_grid(a.groups ? a.n_groups : a.n_chunks, grid), kBlock,
                      lds_for_blocks_per_cu(adam_blocks_per_cu<GDT, RC>(a.rs.R)), s, a);
 }
 
@@ -826,6 +905,8 @@ extern "C" int zero_adam_step(const zero_adam_args* p, hipStream_t stream) {
   if (p->step == 0) return fail(ZERO_EINVAL, "%s: step counts from 1", who);
   if (p->begin > p->end) return fail(ZERO_EINVAL, "%s: begin > end", who);
   if (p->n_chunks > 0 && !p->chunks) return fail(ZERO_EINVAL, "%s: chunks is NULL", who);
+  if (!p->groups && p->n_groups != 0)
+    return fail(ZERO_EINVAL, "%s: n_groups given without a group table", who);
   const bool reduced = p->reduced_g != nullptr;
   if (reduced) {
     if (!aligned16(p->reduced_g))
@@ -856,7 +937,7 @@ extern "C" int zero_adam_step(const zero_adam_args* p, hipStream_t stream) {
     return fail(ZERO_EINVAL, "%s: lr, eps, weight_decay and clip_coef must be >= 0", who);
   if (p->beta1 < 0 || p->beta1 >= 1 || p->beta2 < 0 || p->beta2 >= 1)
     return fail(ZERO_EINVAL, "%s: betas must lie in [0, 1)", who);
-  if (p->n_chunks == 0 || p->begin == p->end) return ZERO_OK;
+  if (p->n_chunks == 0 || p->begin == p->end || (p->groups && p->n_groups == 0)) return ZERO_OK;
   if ((rc = begin_launch())) return rc;
 
   // Constants in fp64, each rounded once to fp32.
@@ -875,6 +956,8 @@ extern "C" int zero_adam_step(const zero_adam_args* p, hipStream_t stream) {
   a.c.clip = (float)p->clip_coef;
   a.chunks = p->chunks;
   a.n_chunks = p->n_chunks;
+  a.groups = p->groups;
+  a.n_groups = p->groups ? p->n_groups : 0;
   a.begin = p->begin;
   a.end = p->end;
   a.reduced_g = p->reduced_g;
