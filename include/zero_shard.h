@@ -302,7 +302,8 @@ typedef struct {
  * with constants derived on the host in fp64.
  * Errors: EINVAL (NULL args, step 0, bad dtype/R/alignment/bases, hyper-
  * parameters out of range: lr, wd, eps >= 0, betas in [0, 1), divisor > 0,
- * clip_coef >= 0, all finite); EHIP.  n_chunks == 0 or begin == end is a no-op.
+ * clip_coef >= 0, all finite; n_groups without a group table); EHIP.
+ * n_chunks == 0, begin == end, or a group table with n_groups == 0 is a no-op.
  * -------------------------------------------------------------------------- */
 int zero_adam_step(const zero_adam_args *args, hipStream_t stream);
 
