@@ -162,6 +162,10 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     assert L.zero_adam_step(ct.byref(a), None) == zs.ZERO_EINVAL
     assert b"step" in L.zero_last_error()
     assert L.zero_adam_step(None, None) == zs.ZERO_EINVAL
+    g = zs.AdamArgs()
+    g.step, g.n_groups = 1, 3  # a group count without a group table
+    assert L.zero_adam_step(ct.byref(g), None) == zs.ZERO_EINVAL
+    assert b"group" in L.zero_last_error()
     a.step, a.begin, a.end = 1, 10, 5
     assert L.zero_adam_step(ct.byref(a), None) == zs.ZERO_EINVAL
     a.begin, a.end = 0, 8
