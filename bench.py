@@ -519,13 +519,20 @@ class Stage3Gather:
         self.out = torch.empty(self.gathered, dtype=torch.bfloat16, device="cuda")
         self.spans = zs.zero3_gather_spans(self.numels, R, self.live)
         self.spans_dev = zs.spans_to_device(self.spans)
+        # short spans packed several to a block when that pays (here it does not:
+        # only the norms' 512-element shards are short)
+        groups = zs.zero_span_groups(self.spans, 2)
+        self.n_groups = groups.size - 1
+        self.groups_dev = (torch.from_numpy(groups.astype(np.int64)).to("cuda")
+                           if zs.groups_pay(self.n_groups, self.spans.size) else None)
         self.so = np.concatenate([[0], np.cumsum(self.shard_numel)[:-1]]).astype(np.int64)
         torch.cuda.synchronize()
 
     def run(self):
         import zero_sharded_optimizer_owned_amd as zs
 
-        zs.zero_copy_spans(self.spans_dev, self.spans.size, self.shards, self.out)
+        zs.zero_copy_spans(self.spans_dev, self.spans.size, self.shards, self.out, groups_dev=self.groups_dev,
+                           n_groups=self.n_groups if self.groups_dev is not None else 0)
 
     def expected(self, pos):
         """Generator values at gather-buffer positions (rank r's shard element so_k + j)."""

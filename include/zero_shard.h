@@ -389,6 +389,21 @@ int zero3_partition_spans(const uint64_t *numel, uint32_t n_tensors, uint32_t ra
 #define ZERO_MAX_COPY_SOURCES 128
 
 /* ----------------------------------------------------------------------------
+ * zero_span_groups -- packs runs of short spans into groups that one block of
+ * zero_copy_spans copies together (host only; a layout aid).  As
+ * zero_chunk_groups, with a span's work units being its scalar head
+ * elements, 16-byte vectors and scalar tail elements when source and
+ * destination share their 16-byte phase, else one unit per element.  Small
+ * tensors give short shards (a 4096-element norm over 8 ranks: 512-element
+ * spans), one almost idle block each without groups.
+ * spans[n_spans] in: a host copy of the span table; elem_bytes 2 or 4;
+ * max_group_elems > 0; out/capacity/n_groups as in zero_chunk_groups.
+ * Errors: EINVAL (NULL pointers, bad elem_bytes, max_group_elems 0); ERANGE.
+ * -------------------------------------------------------------------------- */
+int zero_span_groups(const zero_copy_span *spans, uint64_t n_spans, uint32_t elem_bytes,
+                     uint32_t max_group_elems, uint64_t *out, uint64_t capacity, uint64_t *n_groups);
+
+/* ----------------------------------------------------------------------------
  * zero_copy_spans -- dst[span.dst + i] = srcs[span.buf][span.src + i] for every
  * span of a device span table, in one multi-span launch.  The
  * device side of the stage-3 gather (and partition) on one GPU.
@@ -397,13 +412,18 @@ int zero3_partition_spans(const uint64_t *numel, uint32_t n_tensors, uint32_t ra
  *                     element counts; n_srcs <= ZERO_MAX_COPY_SOURCES
  * dst, dst_numel      device destination and its element count
  * elem_bytes          2 (fp16/bf16) or 4 (fp32)
+ * groups, n_groups    optional device group table from zero_span_groups
+ *                     (n_groups + 1 entries): one block per group instead of
+ *                     one per span; NULL and 0 for one block per span.  The
+ *                     copies are the same either way.
  * Spans whose buffer index or extent falls outside these counts are skipped.
  * Errors: EINVAL (NULL pointers with work, bad elem_bytes, n_srcs out of
- * range, pointers not 16-byte aligned); EHIP.
+ * range, pointers not 16-byte aligned, n_groups without a group table); EHIP.
  * -------------------------------------------------------------------------- */
 int zero_copy_spans(const zero_copy_span *spans, uint64_t n_spans, const void *const *srcs,
                     const uint64_t *src_numel, uint32_t n_srcs, void *dst, uint64_t dst_numel,
-                    uint32_t elem_bytes, hipStream_t stream);
+                    uint32_t elem_bytes, const uint64_t *groups, uint64_t n_groups,
+                    hipStream_t stream);
 
 /* ----------------------------------------------------------------------------
  * Measurement.

@@ -312,3 +312,35 @@ def test_chunk_groups_partition_the_table():
     assert int(cnt[0]) == 2  # 8 chunks of 10 elements (3 units each): 6 + 2 under the 64-element bound
     assert L.zero_chunk_groups(ch.ctypes.data, ch.size, 0, None, 0, cnt.ctypes.data) == zs.ZERO_EINVAL
     assert L.zero_chunk_groups(None, 3, 64, None, 0, cnt.ctypes.data) == zs.ZERO_EINVAL
+
+
+def test_span_groups_partition_the_table():
+    """Span groups cover the spans in order; several spans share a group only
+    within 256 work units (vectors of 16 bytes when the phases agree, else
+    single elements) and max_group elements."""
+    rnd = random.Random(12)
+    for _ in range(100):
+        sizes = [rnd.randrange(1, rnd.choice([50, 600, 9000])) for _ in range(rnd.randrange(1, 40))]
+        R = rnd.randrange(1, 9)
+        live = sorted(rnd.sample(range(len(sizes)), rnd.randrange(1, len(sizes) + 1)))
+        sp = zs.zero3_gather_spans(sizes, R, live, max_span=rnd.choice([7, 512, 4096]))
+        eb = rnd.choice([2, 4])
+        V = 16 // eb
+        mg = rnd.choice([64, 4096])
+        g = zs.zero_span_groups(sp, eb, mg)
+        assert g[0] == 0 and g[-1] == sp.size and np.all(np.diff(g.astype(np.int64)) > 0)
+
+        def units(s):
+            ln, src, dst = int(s["len"]), int(s["src"]), int(s["dst"])
+            if (src - dst) % V:
+                return ln
+            head = min(ln, (V - dst % V) % V)
+            return ln - (ln - head) // V * (V - 1)
+
+        for i in range(g.size - 1):
+            part = sp[int(g[i]):int(g[i + 1])]
+            if part.size > 1:
+                assert sum(units(s) for s in part) <= 256 and int(part["len"].sum()) <= mg
+    cnt = np.zeros(1, dtype=np.uint64)
+    assert zs.lib().zero_span_groups(None, 2, 2, 64, None, 0, cnt.ctypes.data) == zs.ZERO_EINVAL
+    assert zs.lib().zero_span_groups(sp.ctypes.data, sp.size, 3, 64, None, 0, cnt.ctypes.data) == zs.ZERO_EINVAL

@@ -24,11 +24,17 @@ def _gpu():
     yield
 
 
+def _groups(spans, code):
+    g = zs.zero_span_groups(spans, 2 if code == BF16 else 4)
+    return dict(groups_dev=torch.from_numpy(g.astype(np.int64)).to(DEV), n_groups=g.size - 1)
+
+
 @pytest.mark.parametrize("code", [BF16, F32])
 @pytest.mark.parametrize("R", [1, 3, 8])
 @pytest.mark.parametrize("max_span", [7, 4096])
-def test_partition_then_gather_matches_oracle(code, R, max_span):
-    sizes = [5, 9, 2, 1000, 4096, 13, 77_777, 64]
+@pytest.mark.parametrize("grouped", [False, True])
+def test_partition_then_gather_matches_oracle(code, R, max_span, grouped):
+    sizes = [5, 9, 2, 1000, 4096, 13, 77_777, 64] + [1 + (31 * k) % 90 for k in range(40)]
     dense = gen(R, synth.STREAM_MASTER, sum(sizes), synth.DIST_NORMAL, 0.02, code)
     dense_dev = to_dev(dense, code)
     shard_numel, resident, _ = zs.zero3_storage(sizes, R)
@@ -37,14 +43,16 @@ def test_partition_then_gather_matches_oracle(code, R, max_span):
     for r in range(R):
         spans = zs.zero3_partition_spans(sizes, R, r, max_span=max_span)
         buf = torch.zeros(resident, dtype=dense_dev.dtype, device=DEV)
-        zs.zero_copy_spans(zs.spans_to_device(spans) if spans.size else None, spans.size, [dense_dev], buf)
+        gk = _groups(spans, code) if grouped and spans.size else {}
+        zs.zero_copy_spans(zs.spans_to_device(spans) if spans.size else None, spans.size, [dense_dev], buf, **gk)
         assert_bits_equal(from_dev(buf), want_shards[r], f"shard of rank {r}")
         shard_devs.append(buf)
-    for live in ([1], [0, 1], [6, 3, 0], list(range(len(sizes)))):
+    for live in ([1], [0, 1], [6, 3, 0], list(range(len(sizes))), list(range(8, len(sizes)))):
         _, _, gathered = zs.zero3_storage(sizes, R, live)
         spans = zs.zero3_gather_spans(sizes, R, live, max_span=max_span)
         out = torch.full((gathered,), 7, dtype=dense_dev.dtype, device=DEV)
-        zs.zero_copy_spans(zs.spans_to_device(spans), spans.size, shard_devs, out)
+        gk = _groups(spans, code) if grouped else {}
+        zs.zero_copy_spans(zs.spans_to_device(spans), spans.size, shard_devs, out, **gk)
         want = oracle.stage3_gather(sizes, R, want_shards, live)
         assert_bits_equal(from_dev(out), want, f"gather of {live}")
 

@@ -31,7 +31,7 @@ EXPORTED = ("zero_last_error", "zero_shard_layout", "zero_chunk_table", "zero_st
             "zero_reduce_owned", "zero_grad_check", "zero_clip_coef", "zero_adam_step",
             "zero_owner_to_dense", "zero_dense_to_owner", "zero3_storage", "zero3_gather_spans",
             "zero3_partition_spans", "zero_copy_spans", "zero_stream_probe",
-            "zero_check_workspace_bytes", "zero_chunk_groups")
+            "zero_check_workspace_bytes", "zero_chunk_groups", "zero_span_groups")
 
 CHUNK_DTYPE = np.dtype([("flat", "<u8"), ("len", "<u4"), ("tensor", "<u4")])
 SPAN_DTYPE = np.dtype([("src", "<u8"), ("dst", "<u8"), ("len", "<u4"), ("buf", "<u4")])
@@ -88,7 +88,8 @@ def load(path: str):
     L.zero3_storage.argtypes = [P, U32, U32, P, U32, P, P, P]
     L.zero3_gather_spans.argtypes = [P, U32, U32, P, U32, U32, P, U64, P]
     L.zero3_partition_spans.argtypes = [P, U32, U32, U32, U32, P, U64, P]
-    L.zero_copy_spans.argtypes = [P, U64, P, P, U32, P, U64, U32, P]
+    L.zero_copy_spans.argtypes = [P, U64, P, P, U32, P, U64, U32, P, U64, P]
+    L.zero_span_groups.argtypes = [P, U64, U32, U32, P, U64, P]
     L.zero_stream_probe.argtypes = [P, U32, P, U32, U64, P]
     L.zero_check_workspace_bytes.argtypes = [U64, P]
     L.zero_chunk_groups.argtypes = [P, U64, U32, P, U64, P]
@@ -143,6 +144,14 @@ def zero_chunk_table(numels: Sequence[int], offsets: Sequence[int], begin: int, 
     _check(lib().zero_chunk_table(_p(n), _p(off), n.size, begin, end, max_chunk,
                                   _p(out) if out.size else None, out.size, _p(count)))
     return out
+
+
+def groups_pay(n_groups: int, n_items: int) -> bool:
+    """Whether a group table is worth its indirection: a group kernel block
+    first reads its group bounds, then its chunks or spans, and that extra
+    dependent load cost 17% on a span copy of long spans.  Packing pays when
+    it at least halves the block count (512-element spans: +84%)."""
+    return 2 * n_groups <= n_items
 
 
 def zero_chunk_groups(chunks: np.ndarray, max_group: int) -> np.ndarray:
@@ -417,8 +426,20 @@ def spans_to_device(spans: np.ndarray, device=None):
     return torch.from_numpy(np.ascontiguousarray(spans).view(np.uint8).copy()).to(device or "cuda")
 
 
-def zero_copy_spans(spans_dev, n_spans: int, srcs, dst) -> None:
-    """dst[span.dst + i] = srcs[span.buf][span.src + i] over a device span table."""
+def zero_span_groups(spans: np.ndarray, elem_bytes: int, max_group: int = DEFAULT_SPAN) -> np.ndarray:
+    """Group table (first span of each group, then len(spans)) packing runs of
+    short spans for zero_copy_spans; uint64, n_groups + 1 entries."""
+    sp = np.ascontiguousarray(spans, dtype=SPAN_DTYPE)
+    count = np.zeros(1, dtype=np.uint64)
+    _check(lib().zero_span_groups(_p(sp), sp.size, elem_bytes, max_group, None, 0, _p(count)))
+    out = np.zeros(int(count[0]) + 1, dtype=np.uint64)
+    _check(lib().zero_span_groups(_p(sp), sp.size, elem_bytes, max_group, _p(out), out.size, _p(count)))
+    return out
+
+
+def zero_copy_spans(spans_dev, n_spans: int, srcs, dst, groups_dev=None, n_groups: int = 0) -> None:
+    """dst[span.dst + i] = srcs[span.buf][span.src + i] over a device span table
+    (optionally packed by a device group table from ``zero_span_groups``)."""
     torch = _torch()
     if not srcs or len(srcs) > ZERO_MAX_COPY_SOURCES:
         raise ValueError(f"between 1 and {ZERO_MAX_COPY_SOURCES} source buffers")
@@ -435,9 +456,17 @@ def zero_copy_spans(spans_dev, n_spans: int, srcs, dst) -> None:
         _dev(spans_dev, "spans")
         if spans_dev.numel() * spans_dev.element_size() < n_spans * SPAN_DTYPE.itemsize:
             raise ValueError("span table smaller than n_spans")
+    gptr = None
+    if groups_dev is not None:
+        _dev(groups_dev, "groups", torch.int64)
+        if groups_dev.numel() < n_groups + 1:
+            raise ValueError("group table smaller than n_groups + 1")
+        gptr = ct.c_void_p(groups_dev.data_ptr())
+    elif n_groups:
+        raise ValueError("n_groups given without a group table")
     _check(lib().zero_copy_spans(ct.c_void_p(spans_dev.data_ptr()) if spans_dev is not None else None,
                                  n_spans, arr, _p(sizes), len(srcs), ct.c_void_p(dst.data_ptr()),
-                                 dst.numel(), dst.element_size(), _stream()))
+                                 dst.numel(), dst.element_size(), gptr, n_groups if gptr else 0, _stream()))
 
 
 def zero_stream_probe(srcs, dsts) -> None:
@@ -482,11 +511,11 @@ class OwnerShard:
         self.chunks = zero_chunk_table(self.numels, self.offsets, self.begin, self.end, max_chunk)
         self.device = torch.device(device or "cuda")
         self.chunks_dev = chunks_to_device(self.chunks, self.device)
-        # short chunks packed several to a block, when that saves blocks
+        # short chunks packed several to a block, when that saves enough blocks
         self.groups = zero_chunk_groups(self.chunks, max_chunk)
         self.n_groups = self.groups.size - 1
         self.groups_dev = None
-        if self.n_groups < self.chunks.size:
+        if groups_pay(self.n_groups, self.chunks.size):
             self.groups_dev = torch.from_numpy(self.groups.astype(np.int64)).to(self.device)
         self.n_real = int(self.chunks["len"].sum()) if self.chunks.size else 0
         self.align = align

@@ -68,6 +68,8 @@ __global__ void __launch_bounds__(kBlock) dense_kernel(const DenseArgs a) {
 struct SpanArgs {
   const zero_copy_span* spans;
   uint64_t n_spans;
+  const uint64_t* groups;  // [n_groups + 1] first span of each block's work, or NULL
+  uint64_t n_groups;
   const void* src[ZERO_MAX_COPY_SOURCES];
   uint64_t src_numel[ZERO_MAX_COPY_SOURCES];
   uint32_t n_srcs;
@@ -75,51 +77,139 @@ struct SpanArgs {
   uint64_t dst_numel;
 };
 
-// One block per span (grid stride past the grid).  When source and
-// destination share their phase within a 16-byte vector, the body moves as
-// 128-bit vectors (consecutive threads on consecutive vectors, up to four per
-// thread in flight) between scalar head and tail pieces; otherwise threads
-// copy single elements.  Spans that do not fit their buffers are skipped.
+// Whether a span lies inside its source and the destination.
+__device__ __forceinline__ bool span_fits(const SpanArgs& a, const zero_copy_span& sp) {
+  if (sp.buf >= a.n_srcs) return false;
+  const uint64_t len = sp.len, sn = a.src_numel[sp.buf];
+  return !(sp.src > sn || len > sn - sp.src || sp.dst > a.dst_numel || len > a.dst_numel - sp.dst);
+}
+
+// One span by one block.  When source and destination share their phase
+// within a 16-byte vector, the body moves as 128-bit vectors (consecutive
+// threads on consecutive vectors, up to four per thread in flight) between
+// scalar head and tail pieces; otherwise threads copy single elements.  Spans
+// that do not fit their buffers are skipped.
+template <typename T>
+__device__ __forceinline__ void span_one(const SpanArgs& a, const zero_copy_span sp, uint64_t t) {
+  constexpr uint64_t V = 16 / sizeof(T);
+  if (!span_fits(a, sp)) return;
+  const uint64_t len = sp.len;
+  const T* s = static_cast<const T*>(a.src[sp.buf]) + sp.src;
+  T* d = static_cast<T*>(a.dst) + sp.dst;
+  if ((sp.src - sp.dst) % V == 0) {
+    const uint64_t head = min(len, (V - sp.dst % V) % V);
+    const uint64_t body = (len - head) / V;
+    const uint64_t tail0 = head + body * V;
+    if (t < head) d[t] = s[t];
+    if (t < len - tail0) d[tail0 + t] = s[tail0 + t];
+    const uint4* sv = reinterpret_cast<const uint4*>(s + head);
+    uint4* dv = reinterpret_cast<uint4*>(d + head);
+    for (uint64_t v = t; v < body; v += 4 * kBlock) {
+      uint4 x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (v + kBlock * j < body) x[j] = sv[v + kBlock * j];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (v + kBlock * j < body) dv[v + kBlock * j] = x[j];
+    }
+  } else {
+    for (uint64_t i = t; i < len; i += 4 * kBlock) {
+      T x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (i + kBlock * j < len) x[j] = s[i + kBlock * j];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (i + kBlock * j < len) d[i + kBlock * j] = x[j];
+    }
+  }
+}
+
+// One block per span (grid stride past the grid).
 template <typename T>
 __global__ void __launch_bounds__(kBlock) span_kernel(const SpanArgs a) {
+  for (uint64_t c = blockIdx.x; c < a.n_spans; c += gridDim.x) span_one<T>(a, a.spans[c], threadIdx.x);
+}
+
+// Several short spans by one block.  Each span is cut into work units --
+// scalar head elements, 128-bit vectors, scalar tail elements; a span whose
+// source and destination phases differ is all scalar units -- and the
+// block's threads take the units of all its spans together, finding a unit's
+// span by binary search over the prefix sums of the unit counts (spans taken
+// kBlock at a time).
+template <typename T>
+__device__ void span_packed(const SpanArgs& a, uint64_t c0, uint64_t c1, uint32_t t) {
   constexpr uint64_t V = 16 / sizeof(T);
-  const uint64_t t = threadIdx.x;
-  for (uint64_t c = blockIdx.x; c < a.n_spans; c += gridDim.x) {
-    const zero_copy_span sp = a.spans[c];
-    if (sp.buf >= a.n_srcs) continue;
-    const uint64_t len = sp.len;
-    const uint64_t sn = a.src_numel[sp.buf];
-    if (sp.src > sn || len > sn - sp.src || sp.dst > a.dst_numel || len > a.dst_numel - sp.dst) continue;
-    const T* s = static_cast<const T*>(a.src[sp.buf]) + sp.src;
-    T* d = static_cast<T*>(a.dst) + sp.dst;
-    if ((sp.src - sp.dst) % V == 0) {
-      const uint64_t head = min(len, (V - sp.dst % V) % V);
-      const uint64_t body = (len - head) / V;
-      const uint64_t tail0 = head + body * V;
-      if (t < head) d[t] = s[t];
-      if (t < len - tail0) d[tail0 + t] = s[tail0 + t];
-      const uint4* sv = reinterpret_cast<const uint4*>(s + head);
-      uint4* dv = reinterpret_cast<uint4*>(d + head);
-      for (uint64_t v = t; v < body; v += 4 * kBlock) {
-        uint4 x[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (v + kBlock * j < body) x[j] = sv[v + kBlock * j];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (v + kBlock * j < body) dv[v + kBlock * j] = x[j];
-      }
-    } else {
-      for (uint64_t i = t; i < len; i += 4 * kBlock) {
-        T x[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (i + kBlock * j < len) x[j] = s[i + kBlock * j];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (i + kBlock * j < len) d[i + kBlock * j] = x[j];
+  __shared__ const T* s_src[kBlock];
+  __shared__ T* s_dst[kBlock];
+  __shared__ uint32_t s_head[kBlock], s_nvec[kBlock];
+  __shared__ uint32_t s_pre[kBlock + 1];
+  for (uint64_t s0 = c0; s0 < c1; s0 += kBlock) {
+    const uint32_t m = (uint32_t)min((uint64_t)kBlock, c1 - s0);
+    uint32_t units = 0;
+    if (t < m) {
+      const zero_copy_span sp = a.spans[s0 + t];
+      if (span_fits(a, sp)) {
+        const uint64_t len = sp.len;
+        s_src[t] = static_cast<const T*>(a.src[sp.buf]) + sp.src;
+        s_dst[t] = static_cast<T*>(a.dst) + sp.dst;
+        uint64_t head = len, nvec = 0;
+        if ((sp.src - sp.dst) % V == 0) {
+          head = min(len, (V - sp.dst % V) % V);
+          nvec = (len - head) / V;
+        }
+        s_head[t] = (uint32_t)head;
+        s_nvec[t] = (uint32_t)nvec;
+        units = (uint32_t)(len - nvec * (V - 1));
       }
     }
+    s_pre[t + 1] = units;
+    if (t == 0) s_pre[0] = 0;
+    __syncthreads();
+    for (uint32_t d = 1; d < kBlock; d <<= 1) {
+      const uint32_t x = t + 1 > d ? s_pre[t + 1 - d] : 0u;
+      __syncthreads();
+      s_pre[t + 1] += x;
+      __syncthreads();
+    }
+    const uint32_t total = s_pre[m];
+    for (uint32_t u = t; u < total; u += kBlock) {
+      uint32_t lo = 0, hi = m;
+      while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) / 2;
+        if (s_pre[mid] <= u) lo = mid;
+        else hi = mid;
+      }
+      const uint32_t r = u - s_pre[lo];
+      const uint32_t head = s_head[lo], nvec = s_nvec[lo];
+      const T* src = s_src[lo];
+      T* dst = s_dst[lo];
+      if (r < head) {
+        dst[r] = src[r];
+      } else if (r < head + nvec) {
+        const uint64_t e = head + V * (uint64_t)(r - head);
+        *reinterpret_cast<uint4*>(dst + e) = *reinterpret_cast<const uint4*>(src + e);
+      } else {
+        const uint64_t e = head + V * (uint64_t)nvec + (r - head - nvec);
+        dst[e] = src[e];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// One block per group of the span group table: one long span, or several
+// short ones packed together.
+template <typename T>
+__global__ void __launch_bounds__(kBlock) span_group_kernel(const SpanArgs a) {
+  const uint32_t t = threadIdx.x;
+  for (uint64_t w = blockIdx.x; w < a.n_groups; w += gridDim.x) {
+    const uint64_t c0 = a.groups[w];
+    const uint64_t c1 = min(a.groups[w + 1], a.n_spans);
+    if (c1 <= c0) continue;
+    if (c1 - c0 == 1) span_one<T>(a, a.spans[c0], t);
+    else span_packed<T>(a, c0, c1, t);
   }
 }
 
@@ -184,11 +274,13 @@ extern "C" int zero_dense_to_owner(const zero_chunk* chunks, uint64_t n_chunks, 
 
 extern "C" int zero_copy_spans(const zero_copy_span* spans, uint64_t n_spans, const void* const* srcs,
                                const uint64_t* src_numel, uint32_t n_srcs, void* dst,
-                               uint64_t dst_numel, uint32_t elem_bytes, hipStream_t stream) {
+                               uint64_t dst_numel, uint32_t elem_bytes, const uint64_t* groups,
+                               uint64_t n_groups, hipStream_t stream) {
   static const char* who = "zero_copy_spans";
   clear_error();
   if (elem_bytes != 2 && elem_bytes != 4) return fail(ZERO_EINVAL, "%s: elem_bytes must be 2 or 4", who);
-  if (n_spans == 0) return ZERO_OK;
+  if (!groups && n_groups != 0) return fail(ZERO_EINVAL, "%s: n_groups given without a group table", who);
+  if (n_spans == 0 || (groups && n_groups == 0)) return ZERO_OK;
   if (!spans || !dst) return fail(ZERO_EINVAL, "%s: NULL spans or dst", who);
   if (n_srcs == 0 || n_srcs > ZERO_MAX_COPY_SOURCES)
     return fail(ZERO_EINVAL, "%s: n_srcs = %u outside [1, %d]", who, n_srcs, ZERO_MAX_COPY_SOURCES);
@@ -207,11 +299,19 @@ extern "C" int zero_copy_spans(const zero_copy_span* spans, uint64_t n_spans, co
   a.n_srcs = n_srcs;
   a.dst = dst;
   a.dst_numel = dst_numel;
+  a.groups = groups;
+  a.n_groups = groups ? n_groups : 0;
   int rc = begin_launch();
   if (rc) return rc;
-  if (elem_bytes == 2)
+  if (groups) {
+    if (elem_bytes == 2)
+      hipLaunchKernelGGL(span_group_kernel<uint16_t>, chunk_grid(n_groups, 0), kBlock, 0, stream, a);
+    else
+      hipLaunchKernelGGL(span_group_kernel<uint32_t>, chunk_grid(n_groups, 0), kBlock, 0, stream, a);
+  } else if (elem_bytes == 2) {
     hipLaunchKernelGGL(span_kernel<uint16_t>, chunk_grid(n_spans, 0), kBlock, 0, stream, a);
-  else
+  } else {
     hipLaunchKernelGGL(span_kernel<uint32_t>, chunk_grid(n_spans, 0), kBlock, 0, stream, a);
+  }
   return launch_status(who);
 }

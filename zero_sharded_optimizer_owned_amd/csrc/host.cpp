@@ -119,6 +119,37 @@ extern "C" int zero_chunk_table(const uint64_t* numel, const uint64_t* tensor_of
   return ZERO_OK;
 }
 
+namespace {
+// Greedy grouping shared by the chunk and span group builders: consecutive
+// items go into one group while their work units total at most 256 (one per
+// thread of a block) and their elements at most max_elems; an item of more
+// than 256 units is a group of its own.  `units(i)` and `elems(i)` describe
+// item i.  Writes group starts and the sentinel n, returns the group count.
+template <typename U, typename E>
+uint64_t greedy_groups(uint64_t n, uint64_t max_elems, U units, E elems, uint64_t* out,
+                       uint64_t capacity) {
+  const uint64_t kUnits = 256;
+  uint64_t g = 0;
+  for (uint64_t i = 0; i < n;) {
+    if (out && g < capacity) out[g] = i;
+    ++g;
+    uint64_t u = units(i), e = elems(i), j = i + 1;
+    if (u <= kUnits) {
+      while (j < n) {
+        const uint64_t uj = units(j);
+        if (u + uj > kUnits || e + elems(j) > max_elems) break;
+        u += uj;
+        e += elems(j);
+        ++j;
+      }
+    }
+    i = j;
+  }
+  if (out && g < capacity) out[g] = n;  // sentinel
+  return g;
+}
+}  // namespace
+
 extern "C" int zero_chunk_groups(const zero_chunk* chunks, uint64_t n_chunks, uint32_t max_group_elems,
                                  uint64_t* out, uint64_t capacity, uint64_t* n_groups) {
   zs::clear_error();
@@ -135,28 +166,46 @@ extern "C" int zero_chunk_groups(const zero_chunk* chunks, uint64_t n_chunks, ui
     if (a1 < a0) a1 = a0;
     return (a0 - f0) + (a1 - a0) / 8 + (f1 - a1);
   };
-  const uint64_t kUnits = 256;  // one unit per thread of a 256-thread block
-  uint64_t g = 0;
-  for (uint64_t i = 0; i < n_chunks;) {
-    if (out && g < capacity) out[g] = i;
-    ++g;
-    uint64_t u = units(chunks[i]), elems = chunks[i].len, j = i + 1;
-    if (u <= kUnits) {
-      while (j < n_chunks) {
-        const uint64_t uj = units(chunks[j]);
-        if (u + uj > kUnits || elems + chunks[j].len > max_group_elems) break;
-        u += uj;
-        elems += chunks[j].len;
-        ++j;
-      }
-    }
-    i = j;
-  }
-  if (out && g < capacity) out[g] = n_chunks;  // sentinel
+  auto cunits = [&](uint64_t i) { return units(chunks[i]); };
+  auto celems = [&](uint64_t i) -> uint64_t { return chunks[i].len; };
+  const uint64_t g = greedy_groups(n_chunks, max_group_elems, cunits, celems, out, capacity);
   *n_groups = g;
   if (out == nullptr && capacity == 0) return ZERO_OK;
   if (g + 1 > capacity)
     return fail(ZERO_ERANGE, "zero_chunk_groups: %llu entries needed, capacity %llu",
+                (unsigned long long)(g + 1), (unsigned long long)capacity);
+  return ZERO_OK;
+}
+
+
+extern "C" int zero_span_groups(const zero_copy_span* spans, uint64_t n_spans, uint32_t elem_bytes,
+                                uint32_t max_group_elems, uint64_t* out, uint64_t capacity,
+                                uint64_t* n_groups) {
+  zs::clear_error();
+  if (!n_groups) return fail(ZERO_EINVAL, "zero_span_groups: n_groups is NULL");
+  if (n_spans > 0 && !spans) return fail(ZERO_EINVAL, "zero_span_groups: spans is NULL");
+  if (elem_bytes != 2 && elem_bytes != 4)
+    return fail(ZERO_EINVAL, "zero_span_groups: elem_bytes must be 2 or 4");
+  if (max_group_elems == 0) return fail(ZERO_EINVAL, "zero_span_groups: max_group_elems must be > 0");
+  if (capacity > 0 && !out) return fail(ZERO_EINVAL, "zero_span_groups: out is NULL");
+  const uint64_t V = 16 / elem_bytes;
+  // units: scalar head, vectors, scalar tail when source and destination share
+  // their 16-byte phase, else one unit per element
+  auto units = [&](uint64_t i) -> uint64_t {
+    const zero_copy_span& sp = spans[i];
+    const uint64_t len = sp.len;
+    if ((sp.src - sp.dst) % V != 0) return len;
+    uint64_t head = (V - sp.dst % V) % V;
+    if (head > len) head = len;
+    const uint64_t nvec = (len - head) / V;
+    return len - nvec * (V - 1);
+  };
+  auto elems = [&](uint64_t i) -> uint64_t { return spans[i].len; };
+  const uint64_t g = greedy_groups(n_spans, max_group_elems, units, elems, out, capacity);
+  *n_groups = g;
+  if (out == nullptr && capacity == 0) return ZERO_OK;
+  if (g + 1 > capacity)
+    return fail(ZERO_ERANGE, "zero_span_groups: %llu entries needed, capacity %llu",
                 (unsigned long long)(g + 1), (unsigned long long)capacity);
   return ZERO_OK;
 }
