@@ -393,7 +393,8 @@ int zero3_partition_spans(const uint64_t *numel, uint32_t n_tensors, uint32_t ra
  * zero_copy_spans copies together (host only; a layout aid).  As
  * zero_chunk_groups, with a span's work units being its scalar head
  * elements, 16-byte vectors and scalar tail elements when source and
- * destination share their 16-byte phase, else one unit per element.  Small
+ * destination share their 16-byte phase, else one unit per element, and at
+ * most 2048 units (eight per thread) in a group of several spans.  Small
  * tensors give short shards (a 4096-element norm over 8 ranks: 512-element
  * spans), one almost idle block each without groups.
  * spans[n_spans] in: a host copy of the span table; elem_bytes 2 or 4;

@@ -316,7 +316,7 @@ def test_chunk_groups_partition_the_table():
 
 def test_span_groups_partition_the_table():
     """Span groups cover the spans in order; several spans share a group only
-    within 256 work units (vectors of 16 bytes when the phases agree, else
+    within 2048 work units (vectors of 16 bytes when the phases agree, else
     single elements) and max_group elements."""
     rnd = random.Random(12)
     for _ in range(100):
@@ -340,7 +340,7 @@ def test_span_groups_partition_the_table():
         for i in range(g.size - 1):
             part = sp[int(g[i]):int(g[i + 1])]
             if part.size > 1:
-                assert sum(units(s) for s in part) <= 256 and int(part["len"].sum()) <= mg
+                assert sum(units(s) for s in part) <= 2048 and int(part["len"].sum()) <= mg
     cnt = np.zeros(1, dtype=np.uint64)
     assert zs.lib().zero_span_groups(None, 2, 2, 64, None, 0, cnt.ctypes.data) == zs.ZERO_EINVAL
     assert zs.lib().zero_span_groups(sp.ctypes.data, sp.size, 3, 64, None, 0, cnt.ctypes.data) == zs.ZERO_EINVAL
