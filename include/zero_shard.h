@@ -326,19 +326,26 @@ int zero_adam_step(const zero_adam_args *args, hipStream_t stream);
  * the same dense index for every element, and that is how the kernel
  * computes it.)
  * chunks[n_chunks]            device: the owner's chunk table
+ * groups, n_groups            optional device group table from zero_chunk_groups
+ *                             (n_groups + 1 entries): one block per group, the
+ *                             short chunks of a group copied together; NULL
+ *                             and 0 for one block per chunk
  * tensor_offset, dense_offset device uint64 [n_tensors]: flat and dense start of
  *                             each tensor (dense_offset[k] = sum of numel[j<k])
  * owner                       device fp32, at least end - owner_base elements
  * dense                       device fp32 [dense_total]
  * Chunks naming a tensor >= n_tensors, and dense indices >= dense_total, are
  * skipped.  Errors: EINVAL (NULL pointers with work to do, begin > end,
- * owner_base > begin, misaligned fp32 pointers); EHIP.
+ * owner_base > begin, misaligned fp32 pointers, n_groups without a group
+ * table); EHIP.
  * -------------------------------------------------------------------------- */
-int zero_owner_to_dense(const zero_chunk *chunks, uint64_t n_chunks, uint64_t begin, uint64_t end,
+int zero_owner_to_dense(const zero_chunk *chunks, uint64_t n_chunks, const uint64_t *groups,
+                        uint64_t n_groups, uint64_t begin, uint64_t end,
                         const uint64_t *tensor_offset, const uint64_t *dense_offset,
                         uint32_t n_tensors, const float *owner, uint64_t owner_base, float *dense,
                         uint64_t dense_total, hipStream_t stream);
-int zero_dense_to_owner(const zero_chunk *chunks, uint64_t n_chunks, uint64_t begin, uint64_t end,
+int zero_dense_to_owner(const zero_chunk *chunks, uint64_t n_chunks, const uint64_t *groups,
+                        uint64_t n_groups, uint64_t begin, uint64_t end,
                         const uint64_t *tensor_offset, const uint64_t *dense_offset,
                         uint32_t n_tensors, const float *dense, uint64_t dense_total, float *owner,
                         uint64_t owner_base, hipStream_t stream);

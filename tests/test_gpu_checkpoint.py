@@ -32,9 +32,15 @@ def _gpu():
     yield
 
 
-def test_export_import_matches_oracle():
-    numels, R, A = [5, 17, 1, 64, 9, 3000, 777, 4096], 3, 8
-    shards = [zs.OwnerShard(numels, R, r, align=A, max_chunk=64, device=DEV) for r in range(R)]
+@pytest.mark.parametrize("numels,R,A,max_chunk", [
+    ([5, 17, 1, 64, 9, 3000, 777, 4096], 3, 8, 64),
+    # short padded tensors: the owners copy through packed chunk groups
+    ([1 + (37 * k) % 150 for k in range(300)], 3, 64, 2048),
+])
+def test_export_import_matches_oracle(numels, R, A, max_chunk):
+    shards = [zs.OwnerShard(numels, R, r, align=A, max_chunk=max_chunk, device=DEV) for r in range(R)]
+    if A == 64:
+        assert all(sh.groups_dev is not None for sh in shards)
     arrays = []
     for r, sh in enumerate(shards):
         a = gen(r, synth.STREAM_MASTER, max(8, sh.local_size), synth.DIST_NORMAL, 0.02, F32)

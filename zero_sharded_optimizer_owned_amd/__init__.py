@@ -83,8 +83,8 @@ def load(path: str):
     L.zero_grad_check.argtypes = [P, U64, P, P, P, ct.c_size_t, P]
     L.zero_clip_coef.argtypes = [D, D, D, ct.POINTER(F)]
     L.zero_adam_step.argtypes = [ct.POINTER(AdamArgs), P]
-    L.zero_owner_to_dense.argtypes = [P, U64, U64, U64, P, P, U32, P, U64, P, U64, P]
-    L.zero_dense_to_owner.argtypes = [P, U64, U64, U64, P, P, U32, P, U64, P, U64, P]
+    L.zero_owner_to_dense.argtypes = [P, U64, P, U64, U64, U64, P, P, U32, P, U64, P, U64, P]
+    L.zero_dense_to_owner.argtypes = [P, U64, P, U64, U64, U64, P, P, U32, P, U64, P, U64, P]
     L.zero3_storage.argtypes = [P, U32, U32, P, U32, P, P, P]
     L.zero3_gather_spans.argtypes = [P, U32, U32, P, U32, U32, P, U64, P]
     L.zero3_partition_spans.argtypes = [P, U32, U32, U32, U32, P, U64, P]
@@ -345,8 +345,19 @@ def zero_adam_step(*, chunks_dev, n_chunks: int, begin: int, end: int, master, e
     del keep
 
 
+def _group_ptr(groups_dev, n_groups):
+    if groups_dev is None:
+        if n_groups:
+            raise ValueError("n_groups given without a group table")
+        return None, 0
+    _dev(groups_dev, "groups", _torch().int64)
+    if groups_dev.numel() < n_groups + 1:
+        raise ValueError("group table smaller than n_groups + 1")
+    return ct.c_void_p(groups_dev.data_ptr()), n_groups
+
+
 def _dense_call(name, chunks_dev, n_chunks, begin, end, tensor_offset_dev, dense_offset_dev, owner,
-                owner_base, dense):
+                owner_base, dense, groups_dev=None, n_groups=0):
     torch = _torch()
     _dev(owner, "owner", torch.float32)
     _dev(dense, "dense", torch.float32)
@@ -358,8 +369,9 @@ def _dense_call(name, chunks_dev, n_chunks, begin, end, tensor_offset_dev, dense
     if chunks_dev is not None and chunks_dev.numel() * chunks_dev.element_size() < n_chunks * CHUNK_DTYPE.itemsize:
         raise ValueError("chunk table smaller than n_chunks")
     L = lib()
-    common = (ct.c_void_p(chunks_dev.data_ptr()) if chunks_dev is not None else None, n_chunks, begin, end,
-              ct.c_void_p(tensor_offset_dev.data_ptr()), ct.c_void_p(dense_offset_dev.data_ptr()),
+    gptr, ng = _group_ptr(groups_dev, n_groups)
+    common = (ct.c_void_p(chunks_dev.data_ptr()) if chunks_dev is not None else None, n_chunks, gptr, ng,
+              begin, end, ct.c_void_p(tensor_offset_dev.data_ptr()), ct.c_void_p(dense_offset_dev.data_ptr()),
               tensor_offset_dev.numel())
     if name == "zero_owner_to_dense":
         _check(L.zero_owner_to_dense(*common, ct.c_void_p(owner.data_ptr()), owner_base,
@@ -370,17 +382,17 @@ def _dense_call(name, chunks_dev, n_chunks, begin, end, tensor_offset_dev, dense
 
 
 def zero_owner_to_dense(chunks_dev, n_chunks, begin, end, tensor_offset_dev, dense_offset_dev, owner,
-                        owner_base, dense) -> None:
+                        owner_base, dense, groups_dev=None, n_groups: int = 0) -> None:
     """dense[dense_offset[k] + f - tensor_offset[k]] = owner[f - owner_base] for the owner's real f."""
     _dense_call("zero_owner_to_dense", chunks_dev, n_chunks, begin, end, tensor_offset_dev,
-                dense_offset_dev, owner, owner_base, dense)
+                dense_offset_dev, owner, owner_base, dense, groups_dev, n_groups)
 
 
 def zero_dense_to_owner(chunks_dev, n_chunks, begin, end, tensor_offset_dev, dense_offset_dev, dense,
-                        owner, owner_base) -> None:
+                        owner, owner_base, groups_dev=None, n_groups: int = 0) -> None:
     """owner[f - owner_base] = dense[dense_offset[k] + f - tensor_offset[k]] for the owner's real f."""
     _dense_call("zero_dense_to_owner", chunks_dev, n_chunks, begin, end, tensor_offset_dev,
-                dense_offset_dev, owner, owner_base, dense)
+                dense_offset_dev, owner, owner_base, dense, groups_dev, n_groups)
 
 
 # ---------------------------------------------------------------- ZeRO-3 partition / gather
@@ -456,17 +468,10 @@ def zero_copy_spans(spans_dev, n_spans: int, srcs, dst, groups_dev=None, n_group
         _dev(spans_dev, "spans")
         if spans_dev.numel() * spans_dev.element_size() < n_spans * SPAN_DTYPE.itemsize:
             raise ValueError("span table smaller than n_spans")
-    gptr = None
-    if groups_dev is not None:
-        _dev(groups_dev, "groups", torch.int64)
-        if groups_dev.numel() < n_groups + 1:
-            raise ValueError("group table smaller than n_groups + 1")
-        gptr = ct.c_void_p(groups_dev.data_ptr())
-    elif n_groups:
-        raise ValueError("n_groups given without a group table")
+    gptr, ng = _group_ptr(groups_dev, n_groups)
     _check(lib().zero_copy_spans(ct.c_void_p(spans_dev.data_ptr()) if spans_dev is not None else None,
                                  n_spans, arr, _p(sizes), len(srcs), ct.c_void_p(dst.data_ptr()),
-                                 dst.numel(), dst.element_size(), gptr, n_groups if gptr else 0, _stream()))
+                                 dst.numel(), dst.element_size(), gptr, ng, _stream()))
 
 
 def zero_stream_probe(srcs, dsts) -> None:
@@ -524,6 +529,11 @@ class OwnerShard:
         self.tensor_offset_dev = torch.from_numpy(self.offsets.astype(np.int64)).to(self.device)
         self.dense_offset_dev = torch.from_numpy(dense_off).to(self.device)
 
+    def _group_args(self) -> dict:
+        if self.groups_dev is None:
+            return {}
+        return {"groups_dev": self.groups_dev, "n_groups": self.n_groups}
+
     def alloc_state(self):
         torch = _torch()
         mk = lambda: torch.zeros(max(8, self.local_size), dtype=torch.float32, device=self.device)
@@ -538,19 +548,19 @@ class OwnerShard:
                        exp_avg_sq=self.exp_avg_sq, local_base=self.local_base, step=step,
                        rank_grads=rank_grads, grad_base=grad_base, divisor=divisor,
                        reduced_g=reduced_g, param16=param16, param_base=param_base,
-                       groups_dev=self.groups_dev, n_groups=self.n_groups if self.groups_dev is not None else 0,
+                       **self._group_args(),
                        clip_coef=clip_coef, grid_blocks=grid_blocks, **hyper)
 
     # -- export / import of fp32 shard data in the dense per-tensor layout
     def to_dense(self, owner_array, dense) -> None:
         """Write this owner's real elements of an owner-local fp32 array into dense weights."""
         zero_owner_to_dense(self.chunks_dev, self.chunks.size, self.begin, self.end, self.tensor_offset_dev,
-                            self.dense_offset_dev, owner_array, self.local_base, dense)
+                            self.dense_offset_dev, owner_array, self.local_base, dense, **self._group_args())
 
     def from_dense(self, dense, owner_array) -> None:
         """Fill this owner's real elements of an owner-local fp32 array from dense weights."""
         zero_dense_to_owner(self.chunks_dev, self.chunks.size, self.begin, self.end, self.tensor_offset_dev,
-                            self.dense_offset_dev, dense, owner_array, self.local_base)
+                            self.dense_offset_dev, dense, owner_array, self.local_base, **self._group_args())
 
     # -- checkpoint of the owner's optimizer state
     def save(self, path: str, step: int) -> None:

@@ -19,6 +19,8 @@ namespace {
 struct DenseArgs {
   const zero_chunk* chunks;
   uint64_t n_chunks;
+  const uint64_t* groups;  // [n_groups + 1] first chunk of each block's work, or NULL
+  uint64_t n_groups;
   uint64_t begin, end;
   const uint64_t* tensor_offset;  // [n_tensors] flat start of each tensor
   const uint64_t* dense_offset;   // [n_tensors] dense start of each tensor
@@ -34,31 +36,95 @@ struct DenseArgs {
 // whose tensor index or position disagrees with the tables are skipped, and
 // no dense index at or past dense_total is touched.
 template <bool TO_DENSE>
-__global__ void __launch_bounds__(kBlock) dense_kernel(const DenseArgs a) {
-  for (uint64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) {
-    const zero_chunk ch = a.chunks[c];
-    if (ch.tensor >= a.n_tensors) continue;
-    const uint64_t toff = a.tensor_offset[ch.tensor];
-    const uint64_t doff = a.dense_offset[ch.tensor];
-    const uint64_t f0 = max(max(ch.flat, a.begin), toff);
-    const uint64_t f1 = min(ch.flat + ch.len, a.end);
-    for (uint64_t f = f0 + threadIdx.x; f < f1; f += 4 * kBlock) {
-      float x[4];
-      uint64_t d[4];
+__device__ __forceinline__ void dense_one(const DenseArgs& a, const zero_chunk ch, uint64_t t) {
+  if (ch.tensor >= a.n_tensors) return;
+  const uint64_t toff = a.tensor_offset[ch.tensor];
+  const uint64_t doff = a.dense_offset[ch.tensor];
+  const uint64_t f0 = max(max(ch.flat, a.begin), toff);
+  const uint64_t f1 = min(ch.flat + ch.len, a.end);
+  for (uint64_t f = f0 + t; f < f1; f += 4 * kBlock) {
+    float x[4];
+    uint64_t d[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint64_t fj = f + kBlock * j;
-        d[j] = fj < f1 ? doff + (fj - toff) : a.dense_total;
-        if (d[j] < a.dense_total) x[j] = TO_DENSE ? a.owner[fj - a.owner_base] : a.dense[d[j]];
-      }
+    for (int j = 0; j < 4; ++j) {
+      const uint64_t fj = f + kBlock * j;
+      d[j] = fj < f1 ? doff + (fj - toff) : a.dense_total;
+      if (d[j] < a.dense_total) x[j] = TO_DENSE ? a.owner[fj - a.owner_base] : a.dense[d[j]];
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (d[j] < a.dense_total) {
-          if (TO_DENSE) a.dense[d[j]] = x[j];
-          else a.owner[f + kBlock * j - a.owner_base] = x[j];
-        }
+    for (int j = 0; j < 4; ++j) {
+      if (d[j] < a.dense_total) {
+        if (TO_DENSE) a.dense[d[j]] = x[j];
+        else a.owner[f + kBlock * j - a.owner_base] = x[j];
       }
     }
+  }
+}
+
+template <bool TO_DENSE>
+__global__ void __launch_bounds__(kBlock) dense_kernel(const DenseArgs a) {
+  for (uint64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x) dense_one<TO_DENSE>(a, a.chunks[c], threadIdx.x);
+}
+
+// Several short chunks by one block: the block's threads take the elements of
+// all its chunks together (thread t on elements t, t + kBlock, ...), finding
+// an element's chunk by binary search over the prefix sums of the chunk
+// lengths (chunks taken kBlock at a time).
+template <bool TO_DENSE>
+__device__ void dense_packed(const DenseArgs& a, uint64_t c0, uint64_t c1, uint32_t t) {
+  __shared__ uint64_t s_f0[kBlock], s_shift[kBlock];
+  __shared__ uint32_t s_pre[kBlock + 1];
+  for (uint64_t s0 = c0; s0 < c1; s0 += kBlock) {
+    const uint32_t m = (uint32_t)min((uint64_t)kBlock, c1 - s0);
+    uint32_t len = 0;
+    if (t < m) {
+      const zero_chunk ch = a.chunks[s0 + t];
+      if (ch.tensor < a.n_tensors) {
+        const uint64_t toff = a.tensor_offset[ch.tensor];
+        const uint64_t f0 = max(max(ch.flat, a.begin), toff);
+        const uint64_t f1 = max(f0, min(ch.flat + ch.len, a.end));
+        s_f0[t] = f0;
+        s_shift[t] = a.dense_offset[ch.tensor] - toff;  // dense index of f = f + shift (wrapping)
+        len = (uint32_t)(f1 - f0);
+      }
+    }
+    s_pre[t + 1] = len;
+    if (t == 0) s_pre[0] = 0;
+    __syncthreads();
+    for (uint32_t d = 1; d < kBlock; d <<= 1) {
+      const uint32_t x = t + 1 > d ? s_pre[t + 1 - d] : 0u;
+      __syncthreads();
+      s_pre[t + 1] += x;
+      __syncthreads();
+    }
+    const uint32_t total = s_pre[m];
+    for (uint32_t e = t; e < total; e += kBlock) {
+      uint32_t lo = 0, hi = m;
+      while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) / 2;
+        if (s_pre[mid] <= e) lo = mid;
+        else hi = mid;
+      }
+      const uint64_t f = s_f0[lo] + (e - s_pre[lo]);
+      const uint64_t d = f + s_shift[lo];
+      if (d < a.dense_total) {
+        if (TO_DENSE) a.dense[d] = a.owner[f - a.owner_base];
+        else a.owner[f - a.owner_base] = a.dense[d];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <bool TO_DENSE>
+__global__ void __launch_bounds__(kBlock) dense_group_kernel(const DenseArgs a) {
+  const uint32_t t = threadIdx.x;
+  for (uint64_t w = blockIdx.x; w < a.n_groups; w += gridDim.x) {
+    const uint64_t c0 = a.groups[w];
+    const uint64_t c1 = min(a.groups[w + 1], a.n_chunks);
+    if (c1 <= c0) continue;
+    if (c1 - c0 == 1) dense_one<TO_DENSE>(a, a.chunks[c0], t);
+    else dense_packed<TO_DENSE>(a, c0, c1, t);
   }
 }
 
@@ -219,24 +285,27 @@ __global__ void __launch_bounds__(kBlock) span_group_kernel(const SpanArgs a) {
 using namespace zs;
 
 namespace {
-int dense_copy(bool to_dense, const zero_chunk* chunks, uint64_t n_chunks, uint64_t begin,
-               uint64_t end, const uint64_t* tensor_offset, const uint64_t* dense_offset,
-               uint32_t n_tensors, float* owner, uint64_t owner_base, float* dense,
-               uint64_t dense_total, hipStream_t stream, const char* who) {
+int dense_copy(bool to_dense, const zero_chunk* chunks, uint64_t n_chunks, const uint64_t* groups,
+               uint64_t n_groups, uint64_t begin, uint64_t end, const uint64_t* tensor_offset,
+               const uint64_t* dense_offset, uint32_t n_tensors, float* owner, uint64_t owner_base,
+               float* dense, uint64_t dense_total, hipStream_t stream, const char* who) {
   clear_error();
   if (begin > end) return fail(ZERO_EINVAL, "%s: begin > end", who);
+  if (!groups && n_groups != 0) return fail(ZERO_EINVAL, "%s: n_groups given without a group table", who);
   if (n_chunks > 0 && (!chunks || !tensor_offset || !dense_offset || !owner || !dense))
     return fail(ZERO_EINVAL, "%s: NULL pointer argument", who);
   if (n_tensors == 0 && n_chunks > 0) return fail(ZERO_EINVAL, "%s: no tensors", who);
   if (owner_base > begin) return fail(ZERO_EINVAL, "%s: owner_base lies above begin", who);
   if ((reinterpret_cast<uintptr_t>(owner) | reinterpret_cast<uintptr_t>(dense)) & 3u)
     return fail(ZERO_EINVAL, "%s: fp32 buffers must be 4-byte aligned", who);
-  if (n_chunks == 0 || begin == end) return ZERO_OK;
+  if (n_chunks == 0 || begin == end || (groups && n_groups == 0)) return ZERO_OK;
   int rc = begin_launch();
   if (rc) return rc;
   DenseArgs a;
   a.chunks = chunks;
   a.n_chunks = n_chunks;
+  a.groups = groups;
+  a.n_groups = groups ? n_groups : 0;
   a.begin = begin;
   a.end = end;
   a.tensor_offset = tensor_offset;
@@ -246,29 +315,35 @@ int dense_copy(bool to_dense, const zero_chunk* chunks, uint64_t n_chunks, uint6
   a.owner_base = owner_base;
   a.dense = dense;
   a.dense_total = dense_total;
-  if (to_dense) hipLaunchKernelGGL(dense_kernel<true>, chunk_grid(n_chunks, 0), kBlock, 0, stream, a);
-  else hipLaunchKernelGGL(dense_kernel<false>, chunk_grid(n_chunks, 0), kBlock, 0, stream, a);
+  if (groups) {
+    if (to_dense) hipLaunchKernelGGL(dense_group_kernel<true>, chunk_grid(n_groups, 0), kBlock, 0, stream, a);
+    else hipLaunchKernelGGL(dense_group_kernel<false>, chunk_grid(n_groups, 0), kBlock, 0, stream, a);
+  } else if (to_dense) {
+    hipLaunchKernelGGL(dense_kernel<true>, chunk_grid(n_chunks, 0), kBlock, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(dense_kernel<false>, chunk_grid(n_chunks, 0), kBlock, 0, stream, a);
+  }
   return launch_status(who);
 }
 }  // namespace
 
-extern "C" int zero_owner_to_dense(const zero_chunk* chunks, uint64_t n_chunks, uint64_t begin,
-                                   uint64_t end, const uint64_t* tensor_offset,
-                                   const uint64_t* dense_offset, uint32_t n_tensors,
-                                   const float* owner, uint64_t owner_base, float* dense,
-                                   uint64_t dense_total, hipStream_t stream) {
-  return dense_copy(true, chunks, n_chunks, begin, end, tensor_offset, dense_offset, n_tensors,
-                    const_cast<float*>(owner), owner_base, dense, dense_total, stream,
+extern "C" int zero_owner_to_dense(const zero_chunk* chunks, uint64_t n_chunks, const uint64_t* groups,
+                                   uint64_t n_groups, uint64_t begin, uint64_t end,
+                                   const uint64_t* tensor_offset, const uint64_t* dense_offset,
+                                   uint32_t n_tensors, const float* owner, uint64_t owner_base,
+                                   float* dense, uint64_t dense_total, hipStream_t stream) {
+  return dense_copy(true, chunks, n_chunks, groups, n_groups, begin, end, tensor_offset, dense_offset,
+                    n_tensors, const_cast<float*>(owner), owner_base, dense, dense_total, stream,
                     "zero_owner_to_dense");
 }
 
-extern "C" int zero_dense_to_owner(const zero_chunk* chunks, uint64_t n_chunks, uint64_t begin,
-                                   uint64_t end, const uint64_t* tensor_offset,
-                                   const uint64_t* dense_offset, uint32_t n_tensors,
-                                   const float* dense, uint64_t dense_total, float* owner,
-                                   uint64_t owner_base, hipStream_t stream) {
-  return dense_copy(false, chunks, n_chunks, begin, end, tensor_offset, dense_offset, n_tensors,
-                    owner, owner_base, const_cast<float*>(dense), dense_total, stream,
+extern "C" int zero_dense_to_owner(const zero_chunk* chunks, uint64_t n_chunks, const uint64_t* groups,
+                                   uint64_t n_groups, uint64_t begin, uint64_t end,
+                                   const uint64_t* tensor_offset, const uint64_t* dense_offset,
+                                   uint32_t n_tensors, const float* dense, uint64_t dense_total,
+                                   float* owner, uint64_t owner_base, hipStream_t stream) {
+  return dense_copy(false, chunks, n_chunks, groups, n_groups, begin, end, tensor_offset, dense_offset,
+                    n_tensors, owner, owner_base, const_cast<float*>(dense), dense_total, stream,
                     "zero_dense_to_owner");
 }
 
