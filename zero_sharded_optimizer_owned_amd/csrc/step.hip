@@ -10,10 +10,11 @@
 //     indices are multiples of 8, so the vectors of all streams start at the
 //     same flat indices and only the ends of a range need scalar peels;
 //   * one block per short contiguous piece: the fused step takes one chunk
-//     of the owner's chunk table per block, the flat-range kernels one piece
-//     of 256 (or 512) vectors, one vector per thread; blocks are dispatched
-//     in order, so the pieces in flight form a narrow window that advances
-//     through every stream (no cross-block synchronisation at all);
+//     of the owner's chunk table per block (or one group of short chunks),
+//     the flat-range kernels one piece of 256 (or 512) vectors, one vector
+//     per thread; blocks are dispatched in order, so the pieces in flight
+//     form a narrow window that advances through every stream (no
+//     cross-block synchronisation at all);
 //   * reductions of the squared norm use fp64 per-thread sums, a wavefront
 //     butterfly (DPP/permute shuffles), an LDS stage per block and fixed
 //     contiguous folds of the per-block partials -- a fixed tree, so the
@@ -49,9 +50,10 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // 8; `Raw` is its storage as loaded (4 VGPRs for 16-bit data, 8 for fp32), so
 // a batch of loads can be in flight before any of them is widened.
 // `load_stream` marks a load as nontemporal (data read exactly once); the
-// fused step uses it for 16-bit rank gradients, and the 16-bit write-back is a
-// nontemporal store.  Measured on shared allocations: +1-3% for those kernels;
-// the same hint on fp32 rank data or on 64-rank reduces made them slower.
+// fused step uses it for 16-bit rank gradients, the flat reduce for 16-bit
+// rank data below 32 ranks, and the 16-bit write-back is a nontemporal store.
+// Measured: +1-6% for those kernels; the same hint on fp32 rank data, on
+// 64-rank reduces or on fp32 stores made them slower or changed nothing.
 // ---------------------------------------------------------------------------
 template <int DT>
 struct Elem;
