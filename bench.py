@@ -50,10 +50,11 @@ def parse():
     ap.add_argument("--chunk", type=int, default=DEFAULT_CHUNK, help="max chunk elements")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--op", default="step", choices=("step", "export", "gather3"),
+    ap.add_argument("--op", default="step", choices=("step", "export", "gather3", "small"),
                     help="step: the owner's optimizer step; export: copy the owner's fp32 master "
                          "into the dense per-tensor layout (checkpoint consolidation); gather3: the "
-                         "ZeRO-3 gather of four Llama-style layers from 8 ranks' bf16 shard buffers")
+                         "ZeRO-3 gather of four Llama-style layers from 8 ranks' bf16 shard buffers; "
+                         "small: the fused step over 2,000,000 padded 100-element tensors (packed chunk groups)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the streaming-probe ceilings measured before the workload")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -609,6 +610,74 @@ def gather3_bench(args, ceil):
     print(json.dumps(line), flush=True)
 
 
+def small_bench(args, ceil):
+    """The fused fp16 step (R=4, AdamW, fp16 write-back) of owner 1 over
+    2,000,000 tensors of 100 elements each, padded to 128 (1.7 GB per step, far
+    above the caches): short chunks, packed several to a block by the chunk
+    group table (one block per chunk is timed beside it)."""
+    import torch
+
+    import synth
+    import zero_sharded_optimizer_owned_amd as zs
+
+    numels, R = [100] * 2_000_000, 4
+    sh = zs.OwnerShard(numels, R, 1, align=64, max_chunk=DEFAULT_CHUNK, device="cuda")
+    sh.alloc_state()
+    lb = sh.local_base
+    fill(sh.master, 7, synth.STREAM_MASTER, 0, lb, synth.DIST_NORMAL, 0.02)
+    fill(sh.exp_avg, 7, synth.STREAM_EXP_AVG, 0, lb, synth.DIST_NORMAL, 5e-4)
+    fill(sh.exp_avg_sq, 7, synth.STREAM_EXP_AVG_SQ, 0, lb, synth.DIST_SQUARE, 1e-4)
+    grads = []
+    for r in range(R):
+        t = torch.empty(sh.end - lb, dtype=torch.float16, device="cuda")
+        fill(t, 7, synth.STREAM_GRAD, r, lb, synth.DIST_NORMAL, 1e-3)
+        grads.append(t)
+    p16 = torch.zeros(sh.padded_total, dtype=torch.float16, device="cuda")
+
+    def step(t, grouped=True):
+        saved = sh.groups_dev
+        if not grouped:
+            sh.groups_dev = None
+        sh.adam_step(step=t, hyper=HP, rank_grads=grads, grad_base=lb, divisor=float(R), param16=p16)
+        sh.groups_dev = saved
+
+    def timed(grouped):
+        for i in range(args.warmup):
+            step(FIRST_STEP + i, grouped)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(args.steps):
+            step(FIRST_STEP + args.warmup + i, grouped)
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / args.steps
+
+    ms_chunk = timed(False)
+    ms = timed(True)
+    n = sh.n_real
+    nbytes = n * (R * 2 + 26)
+    achieved = nbytes / (ms / 1e3) / 1e9
+    line = {
+        "metric": "owned-shard params updated/sec + achieved HBM GB/s (fraction of MI355X peak)",
+        "value": round(n / (ms / 1e3), 1), "unit": "params/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "2,000,000 tensors of 100 elements (padded to 128), R=4, owner 1 of 4, fp16 grads, "
+                               "fp16 write-back; chunk groups", "op": "small", "owned_params": n,
+                   "chunks": int(sh.chunks.size), "groups": int(sh.n_groups)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": None, "kernel": "adam_group_step_f16_f16",
+                     "kernel_ms": round(ms, 4), "bytes_per_launch": nbytes, "elements_per_launch": n,
+                     "bytes_per_element": float(R * 2 + 26)},
+        "one_block_per_chunk": {"ms": round(ms_chunk, 4),
+                                "achieved_gbps": round(nbytes / (ms_chunk / 1e3) / 1e9, 1)},
+    }
+    if ceil:
+        line["ceiling"] = with_ceiling(line["roofline"], ceil)
+    print(json.dumps(line), flush=True)
+
+
 def export_bench(w: Workload, args, ceil):
     """Time the consolidation copy of the owner's fp32 master into dense per-tensor weights."""
     import numpy as np
@@ -680,6 +749,8 @@ def main():
     zs.lib()
     if args.op == "gather3":
         kname = "span_kernel<uint16_t>"
+    elif args.op == "small":
+        kname = "adam_step_f16_f16"
     elif args.op == "export":
         kname = "owner_to_dense"
     elif args.schedule == "per-backward":
@@ -690,6 +761,8 @@ def main():
     ceil = None if args.no_ceiling else ceilings(kname)  # before the workload takes its memory
     if args.op == "gather3":
         return gather3_bench(args, ceil)
+    if args.op == "small":
+        return small_bench(args, ceil)
     if args.calibrate_copy:
         # a plain copy of known size: 2^28 fp32 read + 2^28 fp32 written per launch
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
