@@ -73,10 +73,10 @@ __global__ void __launch_bounds__(kBlock) dense_kernel(const DenseArgs a) {
 template <bool TO_DENSE>
 __device__ void dense_packed(const DenseArgs& a, uint64_t c0, uint64_t c1, uint32_t t) {
   __shared__ uint64_t s_f0[kBlock], s_shift[kBlock];
-  __shared__ uint32_t s_pre[kBlock + 1];
+  __shared__ uint64_t s_pre[kBlock + 1];
   for (uint64_t s0 = c0; s0 < c1; s0 += kBlock) {
     const uint32_t m = (uint32_t)min((uint64_t)kBlock, c1 - s0);
-    uint32_t len = 0;
+    uint64_t len = 0;
     if (t < m) {
       const zero_chunk ch = a.chunks[s0 + t];
       if (ch.tensor < a.n_tensors) {
@@ -85,20 +85,20 @@ __device__ void dense_packed(const DenseArgs& a, uint64_t c0, uint64_t c1, uint3
         const uint64_t f1 = max(f0, min(ch.flat + ch.len, a.end));
         s_f0[t] = f0;
         s_shift[t] = a.dense_offset[ch.tensor] - toff;  // dense index of f = f + shift (wrapping)
-        len = (uint32_t)(f1 - f0);
+        len = f1 - f0;
       }
     }
     s_pre[t + 1] = len;
     if (t == 0) s_pre[0] = 0;
     __syncthreads();
     for (uint32_t d = 1; d < kBlock; d <<= 1) {
-      const uint32_t x = t + 1 > d ? s_pre[t + 1 - d] : 0u;
+      const uint64_t x = t + 1 > d ? s_pre[t + 1 - d] : 0ull;
       __syncthreads();
       s_pre[t + 1] += x;
       __syncthreads();
     }
-    const uint32_t total = s_pre[m];
-    for (uint32_t e = t; e < total; e += kBlock) {
+    const uint64_t total = s_pre[m];
+    for (uint64_t e = t; e < total; e += kBlock) {
       uint32_t lo = 0, hi = m;
       while (hi - lo > 1) {
         const uint32_t mid = (lo + hi) / 2;
@@ -209,11 +209,11 @@ __device__ void span_packed(const SpanArgs& a, uint64_t c0, uint64_t c1, uint32_
   constexpr uint64_t V = 16 / sizeof(T);
   __shared__ const T* s_src[kBlock];
   __shared__ T* s_dst[kBlock];
-  __shared__ uint32_t s_head[kBlock], s_nvec[kBlock];
-  __shared__ uint32_t s_pre[kBlock + 1];
+  __shared__ uint64_t s_head[kBlock], s_nvec[kBlock];
+  __shared__ uint64_t s_pre[kBlock + 1];
   for (uint64_t s0 = c0; s0 < c1; s0 += kBlock) {
     const uint32_t m = (uint32_t)min((uint64_t)kBlock, c1 - s0);
-    uint32_t units = 0;
+    uint64_t units = 0;
     if (t < m) {
       const zero_copy_span sp = a.spans[s0 + t];
       if (span_fits(a, sp)) {
@@ -225,39 +225,39 @@ __device__ void span_packed(const SpanArgs& a, uint64_t c0, uint64_t c1, uint32_
           head = min(len, (V - sp.dst % V) % V);
           nvec = (len - head) / V;
         }
-        s_head[t] = (uint32_t)head;
-        s_nvec[t] = (uint32_t)nvec;
-        units = (uint32_t)(len - nvec * (V - 1));
+        s_head[t] = head;
+        s_nvec[t] = nvec;
+        units = len - nvec * (V - 1);
       }
     }
     s_pre[t + 1] = units;
     if (t == 0) s_pre[0] = 0;
     __syncthreads();
     for (uint32_t d = 1; d < kBlock; d <<= 1) {
-      const uint32_t x = t + 1 > d ? s_pre[t + 1 - d] : 0u;
+      const uint64_t x = t + 1 > d ? s_pre[t + 1 - d] : 0ull;
       __syncthreads();
       s_pre[t + 1] += x;
       __syncthreads();
     }
-    const uint32_t total = s_pre[m];
-    for (uint32_t u = t; u < total; u += kBlock) {
+    const uint64_t total = s_pre[m];
+    for (uint64_t u = t; u < total; u += kBlock) {
       uint32_t lo = 0, hi = m;
       while (hi - lo > 1) {
         const uint32_t mid = (lo + hi) / 2;
         if (s_pre[mid] <= u) lo = mid;
         else hi = mid;
       }
-      const uint32_t r = u - s_pre[lo];
-      const uint32_t head = s_head[lo], nvec = s_nvec[lo];
+      const uint64_t r = u - s_pre[lo];
+      const uint64_t head = s_head[lo], nvec = s_nvec[lo];
       const T* src = s_src[lo];
       T* dst = s_dst[lo];
       if (r < head) {
         dst[r] = src[r];
       } else if (r < head + nvec) {
-        const uint64_t e = head + V * (uint64_t)(r - head);
+        const uint64_t e = head + V * (r - head);
         *reinterpret_cast<uint4*>(dst + e) = *reinterpret_cast<const uint4*>(src + e);
       } else {
-        const uint64_t e = head + V * (uint64_t)nvec + (r - head - nvec);
+        const uint64_t e = head + V * nvec + (r - head - nvec);
         dst[e] = src[e];
       }
     }

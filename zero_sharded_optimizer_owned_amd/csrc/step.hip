@@ -573,20 +573,23 @@ __device__ __forceinline__ void adam_chunk(const AdamArgs& a, const zero_chunk c
 }
 
 // Several short chunks by one block.  Each chunk is cut into work units --
-// its scalar head elements, its 128-bit vectors and its scalar tail elements
-// -- and the block's threads take the units of all its chunks together
-// (thread t on units t, t + kBlock, ...), finding a unit's chunk by binary
-// search over the prefix sums of the unit counts.  The units run the same
-// element and vector routines as above, so the results are identical to one
-// block per chunk.  Chunks are taken kBlock at a time.
+// its 128-bit vectors, and its scalar head and tail elements -- and the
+// block's threads take the units of all its chunks together: first every
+// chunk's vectors, then every chunk's scalar elements, so that a wavefront
+// mostly runs one of the two routines rather than both one after the other
+// (thread t on units t, t + kBlock, ...).  A unit's chunk is found by binary
+// search over the prefix sums of the per-chunk vector (or scalar) counts.
+// The units run the same element and vector routines as one block per chunk,
+// so the results are identical.  Chunks are taken kBlock at a time.
 template <int GDT, int PDT, int RC>
 __device__ void adam_packed(const AdamArgs& a, uint64_t c0, uint64_t c1, uint32_t t) {
   __shared__ uint64_t s_f0[kBlock];
-  __shared__ uint32_t s_head[kBlock], s_nvec[kBlock];
-  __shared__ uint32_t s_pre[kBlock + 1];
+  __shared__ uint32_t s_head[kBlock];
+  __shared__ uint64_t s_nvec[kBlock];
+  __shared__ uint64_t s_pv[kBlock + 1], s_ps[kBlock + 1];  // prefix sums: vectors, scalars
   for (uint64_t s0 = c0; s0 < c1; s0 += kBlock) {
     const uint32_t m = (uint32_t)min((uint64_t)kBlock, c1 - s0);
-    uint32_t units = 0;
+    uint64_t nv = 0, ns = 0;
     if (t < m) {
       const zero_chunk ch = a.chunks[s0 + t];
       const uint64_t f0 = max(ch.flat, a.begin);
@@ -595,37 +598,42 @@ __device__ void adam_packed(const AdamArgs& a, uint64_t c0, uint64_t c1, uint32_
       const uint64_t a1 = max(a0, f1 & ~7ull);
       s_f0[t] = f0;
       s_head[t] = (uint32_t)(a0 - f0);
-      s_nvec[t] = (uint32_t)((a1 - a0) / 8);
-      units = (uint32_t)(a0 - f0) + (uint32_t)((a1 - a0) / 8) + (uint32_t)(f1 - a1);
+      s_nvec[t] = (a1 - a0) / 8;
+      nv = (a1 - a0) / 8;
+      ns = (a0 - f0) + (f1 - a1);
     }
-    // inclusive scan of the unit counts (Hillis-Steele over the block)
-    s_pre[t + 1] = units;
-    if (t == 0) s_pre[0] = 0;
+    // inclusive scans of the vector and scalar counts over the block
+    s_pv[t + 1] = nv;
+    s_ps[t + 1] = ns;
+    if (t == 0) s_pv[0] = s_ps[0] = 0;
     __syncthreads();
     for (uint32_t d = 1; d < kBlock; d <<= 1) {
-      const uint32_t x = t + 1 > d ? s_pre[t + 1 - d] : 0u;
+      const uint64_t xv = t + 1 > d ? s_pv[t + 1 - d] : 0ull;
+      const uint64_t xs = t + 1 > d ? s_ps[t + 1 - d] : 0ull;
       __syncthreads();
-      s_pre[t + 1] += x;
+      s_pv[t + 1] += xv;
+      s_ps[t + 1] += xs;
       __syncthreads();
     }
-    const uint32_t total = s_pre[m];
-    for (uint32_t u = t; u < total; u += kBlock) {
-      uint32_t lo = 0, hi = m;  // the chunk j with s_pre[j] <= u < s_pre[j + 1]
+    const uint64_t n_vec = s_pv[m], n_all = n_vec + s_ps[m];
+    for (uint64_t u = t; u < n_all; u += kBlock) {
+      const bool vec = u < n_vec;
+      const uint64_t k = vec ? u : u - n_vec;
+      const uint64_t* pre = vec ? s_pv : s_ps;
+      uint32_t lo = 0, hi = m;  // the chunk j with pre[j] <= k < pre[j + 1]
       while (hi - lo > 1) {
         const uint32_t mid = (lo + hi) / 2;
-        if (s_pre[mid] <= u) lo = mid;
+        if (pre[mid] <= k) lo = mid;
         else hi = mid;
       }
-      const uint32_t r = u - s_pre[lo];
+      const uint64_t r = k - pre[lo];
       const uint64_t f0 = s_f0[lo];
-      const uint32_t head = s_head[lo], nvec = s_nvec[lo];
-      if (r < head) {
-        adam_one<GDT, PDT, RC>(a, f0 + r);
-      } else if (r < head + nvec) {
-        const uint64_t f[1] = {f0 + head + 8ull * (r - head)};
+      const uint64_t head = s_head[lo], nvec = s_nvec[lo];
+      if (vec) {
+        const uint64_t f[1] = {f0 + head + 8 * r};
         adam_vec<GDT, PDT, RC, 1>(a, f);
       } else {
-        adam_one<GDT, PDT, RC>(a, f0 + head + 8ull * nvec + (r - head - nvec));
+        adam_one<GDT, PDT, RC>(a, r < head ? f0 + r : f0 + head + 8 * nvec + (r - head));
       }
     }
     __syncthreads();  // the next slice reuses the arrays
