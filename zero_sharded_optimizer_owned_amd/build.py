@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(HERE, "libzero_shard.so")
 SOURCES = ("host.cpp", "launch.hip", "step.hip", "copy.hip", "probe.hip")
 # The sources whose kernels make up the optimizer step (hashed to tie counter
 # records to the code they were taken on).
-STEP_SOURCES = ("step.hip", "launch.hip", "launch.h", "internal.h")
+STEP_SOURCES = ("step.hip", "launch.hip", "launch.h", "internal.h", "scan.h")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 HIPCC_FLAGS = [

@@ -9,6 +9,7 @@
 
 #include "internal.h"
 #include "launch.h"
+#include "scan.h"
 
 namespace zs {
 namespace {
@@ -74,6 +75,7 @@ template <bool TO_DENSE>
 __device__ void dense_packed(const DenseArgs& a, uint64_t c0, uint64_t c1, uint32_t t) {
   __shared__ uint64_t s_f0[kBlock], s_shift[kBlock];
   __shared__ uint64_t s_pre[kBlock + 1];
+  __shared__ uint64_t s_wave[kWavesPerBlock];
   for (uint64_t s0 = c0; s0 < c1; s0 += kBlock) {
     const uint32_t m = (uint32_t)min((uint64_t)kBlock, c1 - s0);
     uint64_t len = 0;
@@ -88,15 +90,9 @@ __device__ void dense_packed(const DenseArgs& a, uint64_t c0, uint64_t c1, uint3
         len = f1 - f0;
       }
     }
-    s_pre[t + 1] = len;
+    s_pre[t + 1] = block_inclusive_scan(len, s_wave);
     if (t == 0) s_pre[0] = 0;
     __syncthreads();
-    for (uint32_t d = 1; d < kBlock; d <<= 1) {
-      const uint64_t x = t + 1 > d ? s_pre[t + 1 - d] : 0ull;
-      __syncthreads();
-      s_pre[t + 1] += x;
-      __syncthreads();
-    }
     const uint64_t total = s_pre[m];
     for (uint64_t e = t; e < total; e += kBlock) {
       uint32_t lo = 0, hi = m;
@@ -211,6 +207,7 @@ __device__ void span_packed(const SpanArgs& a, uint64_t c0, uint64_t c1, uint32_
   __shared__ T* s_dst[kBlock];
   __shared__ uint64_t s_head[kBlock], s_nvec[kBlock];
   __shared__ uint64_t s_pre[kBlock + 1];
+  __shared__ uint64_t s_wave[kWavesPerBlock];
   for (uint64_t s0 = c0; s0 < c1; s0 += kBlock) {
     const uint32_t m = (uint32_t)min((uint64_t)kBlock, c1 - s0);
     uint64_t units = 0;
@@ -230,15 +227,9 @@ __device__ void span_packed(const SpanArgs& a, uint64_t c0, uint64_t c1, uint32_
         units = len - nvec * (V - 1);
       }
     }
-    s_pre[t + 1] = units;
+    s_pre[t + 1] = block_inclusive_scan(units, s_wave);
     if (t == 0) s_pre[0] = 0;
     __syncthreads();
-    for (uint32_t d = 1; d < kBlock; d <<= 1) {
-      const uint64_t x = t + 1 > d ? s_pre[t + 1 - d] : 0ull;
-      __syncthreads();
-      s_pre[t + 1] += x;
-      __syncthreads();
-    }
     const uint64_t total = s_pre[m];
     for (uint64_t u = t; u < total; u += kBlock) {
       uint32_t lo = 0, hi = m;

@@ -32,6 +32,7 @@
 
 #include "internal.h"
 #include "launch.h"
+#include "scan.h"
 
 namespace zs {
 namespace {
@@ -587,6 +588,7 @@ __device__ void adam_packed(const AdamArgs& a, uint64_t c0, uint64_t c1, uint32_
   __shared__ uint32_t s_head[kBlock];
   __shared__ uint64_t s_nvec[kBlock];
   __shared__ uint64_t s_pv[kBlock + 1], s_ps[kBlock + 1];  // prefix sums: vectors, scalars
+  __shared__ uint64_t s_wave_v[kWavesPerBlock], s_wave_s[kWavesPerBlock];
   for (uint64_t s0 = c0; s0 < c1; s0 += kBlock) {
     const uint32_t m = (uint32_t)min((uint64_t)kBlock, c1 - s0);
     uint64_t nv = 0, ns = 0;
@@ -602,19 +604,11 @@ __device__ void adam_packed(const AdamArgs& a, uint64_t c0, uint64_t c1, uint32_
       nv = (a1 - a0) / 8;
       ns = (a0 - f0) + (f1 - a1);
     }
-    // inclusive scans of the vector and scalar counts over the block
-    s_pv[t + 1] = nv;
-    s_ps[t + 1] = ns;
+    // prefix sums of the vector and scalar counts over the block
+    s_pv[t + 1] = block_inclusive_scan(nv, s_wave_v);
+    s_ps[t + 1] = block_inclusive_scan(ns, s_wave_s);
     if (t == 0) s_pv[0] = s_ps[0] = 0;
     __syncthreads();
-    for (uint32_t d = 1; d < kBlock; d <<= 1) {
-      const uint64_t xv = t + 1 > d ? s_pv[t + 1 - d] : 0ull;
-      const uint64_t xs = t + 1 > d ? s_ps[t + 1 - d] : 0ull;
-      __syncthreads();
-      s_pv[t + 1] += xv;
-      s_ps[t + 1] += xs;
-      __syncthreads();
-    }
     const uint64_t n_vec = s_pv[m], n_all = n_vec + s_ps[m];
     for (uint64_t u = t; u < n_all; u += kBlock) {
       const bool vec = u < n_vec;
