@@ -667,7 +667,9 @@ def small_bench(args, ceil):
                                "fp16 write-back; chunk groups", "op": "small", "owned_params": n,
                    "chunks": int(sh.chunks.size), "groups": int(sh.n_groups)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": None, "kernel": "adam_group_step_f16_f16",
+                     "frac": round(achieved / PEAK_GBPS, 4),
+                     "traffic": traffic_record("adam_group_step_f16_f16__2M-tensors-100-R4"),
+                     "kernel": "adam_group_step_f16_f16",
                      "kernel_ms": round(ms, 4), "bytes_per_launch": nbytes, "elements_per_launch": n,
                      "bytes_per_element": float(R * 2 + 26)},
         "one_block_per_chunk": {"ms": round(ms_chunk, 4),
@@ -759,10 +761,6 @@ def main():
         kname = {2: "adam_step_f16_f16", 3: "adam_step_bf16_bf16", 4: "reduce_check_f16_r64",
                  5: "accumulate_bf16"}[args.config]
     ceil = None if args.no_ceiling else ceilings(kname)  # before the workload takes its memory
-    if args.op == "gather3":
-        return gather3_bench(args, ceil)
-    if args.op == "small":
-        return small_bench(args, ceil)
     if args.calibrate_copy:
         # a plain copy of known size: 2^28 fp32 read + 2^28 fp32 written per launch
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -771,6 +769,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.op == "gather3":
+        return gather3_bench(args, ceil)
+    if args.op == "small":
+        return small_bench(args, ceil)
     w = Workload(args.config, args.chunk, args.grid, args.schedule)
     if args.op == "export":
         return export_bench(w, args, ceil)

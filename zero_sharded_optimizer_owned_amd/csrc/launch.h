@@ -31,10 +31,10 @@ constexpr uint32_t kMaxChunkGrid = 1u << 23;
 uint32_t chunk_grid(uint64_t n_pieces, uint32_t requested);
 
 // Dynamic LDS bytes that let at most `per_cu` blocks of a kernel reside on one
-// CU at a time (the kernels use no LDS of their own beyond a few bytes; the
-// reservation only caps residency).  0 -- no cap -- when the device cannot
-// give one block that much, or when the query fails.  The device's LDS sizes
-// are queried once per device.
-uint32_t lds_for_blocks_per_cu(uint32_t per_cu);
+// CU at a time, for a kernel whose own arrays take `static_bytes` of LDS (the
+// reservation only caps residency; nothing reads it).  0 -- no cap -- when
+// the device cannot give one block that much, or when the query fails.  The
+// device's LDS sizes are queried once per device.
+uint32_t lds_for_blocks_per_cu(uint32_t per_cu, uint32_t static_bytes);
 
 }  // namespace zs

@@ -24,7 +24,7 @@ int g_lds_cu[kMaxDevices];   // LDS bytes per CU, 0 = not yet queried
 int g_lds_blk[kMaxDevices];  // largest LDS allocation of one block
 }  // namespace
 
-uint32_t lds_for_blocks_per_cu(uint32_t per_cu) {
+uint32_t lds_for_blocks_per_cu(uint32_t per_cu, uint32_t static_bytes) {
   int dev = 0;
   if (per_cu == 0 || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
   int cu = __atomic_load_n(&g_lds_cu[dev], __ATOMIC_ACQUIRE);
@@ -38,10 +38,14 @@ uint32_t lds_for_blocks_per_cu(uint32_t per_cu) {
     __atomic_store_n(&g_lds_blk[dev], blk, __ATOMIC_RELAXED);
     __atomic_store_n(&g_lds_cu[dev], cu, __ATOMIC_RELEASE);
   }
-  // More than a (per_cu + 1)-th of the CU's LDS: per_cu blocks fit, one more does not.
-  const uint64_t bytes = ((uint64_t)cu / (per_cu + 1) + 1024 + 1023) / 1024 * 1024;
-  if (bytes * per_cu > (uint64_t)cu || bytes > (uint64_t)blk) return 0;
-  return (uint32_t)bytes;
+  // A block's whole LDS (its static arrays plus the reservation) must exceed
+  // a (per_cu + 1)-th of the CU's LDS, with a granule of margin: per_cu
+  // blocks fit, one more does not.
+  const uint64_t target = (uint64_t)cu / (per_cu + 1) + 1024;
+  const uint64_t dyn = target > static_bytes ? (target - static_bytes + 1023) / 1024 * 1024 : 0;
+  const uint64_t total = dyn + static_bytes;
+  if (total * per_cu > (uint64_t)cu || total > (uint64_t)blk) return 0;
+  return (uint32_t)dyn;
 }
 
 uint32_t chunk_grid(uint64_t n_pieces, uint32_t requested) {

@@ -582,13 +582,24 @@ __device__ __forceinline__ void adam_chunk(const AdamArgs& a, const zero_chunk c
 // search over the prefix sums of the per-chunk vector (or scalar) counts.
 // The units run the same element and vector routines as one block per chunk,
 // so the results are identical.  Chunks are taken kBlock at a time.
+// The packed path's LDS: per-chunk first element, vector count and head
+// length; prefix sums of the vector and scalar counts; the scans' wave totals.
+struct PackedLds {
+  uint64_t f0[kBlock];
+  uint64_t nvec[kBlock];
+  uint64_t pv[kBlock + 1], ps[kBlock + 1];
+  uint64_t wave_v[kWavesPerBlock], wave_s[kWavesPerBlock];
+  uint32_t head[kBlock];
+};
+
 template <int GDT, int PDT, int RC>
 __device__ void adam_packed(const AdamArgs& a, uint64_t c0, uint64_t c1, uint32_t t) {
-  __shared__ uint64_t s_f0[kBlock];
-  __shared__ uint32_t s_head[kBlock];
-  __shared__ uint64_t s_nvec[kBlock];
-  __shared__ uint64_t s_pv[kBlock + 1], s_ps[kBlock + 1];  // prefix sums: vectors, scalars
-  __shared__ uint64_t s_wave_v[kWavesPerBlock], s_wave_s[kWavesPerBlock];
+  __shared__ PackedLds lds;
+  uint64_t* const s_f0 = lds.f0;
+  uint32_t* const s_head = lds.head;
+  uint64_t* const s_nvec = lds.nvec;
+  uint64_t* const s_pv = lds.pv;
+  uint64_t* const s_ps = lds.ps;
   for (uint64_t s0 = c0; s0 < c1; s0 += kBlock) {
     const uint32_t m = (uint32_t)min((uint64_t)kBlock, c1 - s0);
     uint64_t nv = 0, ns = 0;
@@ -605,8 +616,8 @@ __device__ void adam_packed(const AdamArgs& a, uint64_t c0, uint64_t c1, uint32_
       ns = (a0 - f0) + (f1 - a1);
     }
     // prefix sums of the vector and scalar counts over the block
-    s_pv[t + 1] = block_inclusive_scan(nv, s_wave_v);
-    s_ps[t + 1] = block_inclusive_scan(ns, s_wave_s);
+    s_pv[t + 1] = block_inclusive_scan(nv, lds.wave_v);
+    s_ps[t + 1] = block_inclusive_scan(ns, lds.wave_s);
     if (t == 0) s_pv[0] = s_ps[0] = 0;
     __syncthreads();
     const uint64_t n_vec = s_pv[m], n_all = n_vec + s_ps[m];
@@ -799,7 +810,8 @@ uint32_t adam_blocks_per_cu(uint32_t R) {
 
 template <int GDT, int PDT, int RC>
 void launch_adam_k(const AdamArgs& a, uint32_t grid, hipStream_t s) {
-  const uint32_t lds = lds_for_blocks_per_cu(adam_blocks_per_cu<GDT, RC>(a.rs.R));
+  const uint32_t lds = lds_for_blocks_per_cu(adam_blocks_per_cu<GDT, RC>(a.rs.R),
+                                             a.groups ? (uint32_t)sizeof(PackedLds) : 0u);
   if (a.groups)
     hipLaunchKernelGGL((adam_group_kernel<GDT, PDT, RC>), chunk_grid(a.n_groups, grid), kBlock, lds, s, a);
   else
