@@ -342,6 +342,67 @@ def test_two_pass_with_clip_matches_oracle_and_fused():
         assert_bits_equal(from_dev(a), from_dev(b), "fused vs two-pass")
 
 
+@pytest.mark.parametrize("code", [F16, BF16, F32])
+@pytest.mark.parametrize("R", [1, 2, 6, 8, 16, 17, 24, 37, 256])
+def test_fused_step_every_rank_path(code, R):
+    """The fused step's rank reduce at every code path: fully unrolled counts
+    (1, 2, 8, 16), a batched count with a remainder (6), one full batch plus a
+    remainder (17), several double-buffered batches (24, 37) and the maximum
+    (256).  Against the oracle, and bit-identical to reduce-then-step.  The
+    layout has two owners; the rank count only sets how many buffers are
+    summed."""
+    numels, A = [1000, 37, 5003, 1, 64, 777], 64
+    off, total, b, e = zs.zero_shard_layout(numels, 2, A)
+    begin, end = int(b[1]), int(e[1])
+    lb = begin & ~7
+    grads = _rank_inputs(code, R, total, seed=50 + R)
+    dgr = [to_dev(g, code) for g in grads]
+    size = end - lb
+    w = gen(R, synth.STREAM_MASTER, size, synth.DIST_NORMAL, 0.02, F32)
+    m = gen(R, synth.STREAM_EXP_AVG, size, synth.DIST_NORMAL, 5e-4, F32)
+    v = gen(R, synth.STREAM_EXP_AVG_SQ, size, synth.DIST_SQUARE, 1e-4, F32)
+    chunks = zs.zero_chunk_table(numels, off, begin, end, 512)
+    dch = zs.chunks_to_device(chunks)
+    pcode = BF16 if code == F32 else code
+    dw, dm, dv = to_dev(w, F32), to_dev(m, F32), to_dev(v, F32)
+    dp = torch.zeros(total, dtype=torch.float16 if pcode == F16 else torch.bfloat16, device=DEV)
+    zs.zero_adam_step(chunks_dev=dch, n_chunks=chunks.size, begin=begin, end=end, master=dw, exp_avg=dm,
+                      exp_avg_sq=dv, local_base=lb, step=4, rank_grads=dgr, divisor=float(R), param16=dp, **HP)
+    ranges = oracle.real_ranges(numels, list(off), begin, end)
+    ow, om, ovv = w.copy(), m.copy(), v.copy()
+    p_or = np.zeros(total, dtype=np.uint16)
+    oracle.owner_step(ranges, oracle.hyper(step=4, **HP), ow, om, ovv, lb, grads=grads, gdtype=code,
+                      divisor=float(R), p16=p_or, pdtype=pcode)
+    what = f"R={R}"
+    assert_state_close(from_dev(dw), ow, what + " w")
+    assert_state_close(from_dev(dm), om, what + " m")
+    assert_state_close(from_dev(dv), ovv, what + " v")
+    assert_p16_within_ulp(from_dev(dp), p_or, what + " p16")
+    # reduce-then-step: the flat reduce over the owner range, then AdamW from it
+    g_dev = torch.zeros(size, dtype=torch.float32, device=DEV)
+    zs.zero_reduce_owned(dgr, begin, end - begin, float(R), g_dev, out_base=lb)
+    tw, tm, tv = to_dev(w, F32), to_dev(m, F32), to_dev(v, F32)
+    zs.zero_adam_step(chunks_dev=dch, n_chunks=chunks.size, begin=begin, end=end, master=tw, exp_avg=tm,
+                      exp_avg_sq=tv, local_base=lb, step=4, reduced_g=g_dev, **HP)
+    for a, c in ((dw, tw), (dm, tm), (dv, tv)):
+        assert_bits_equal(from_dev(a), from_dev(c), what + " fused vs two-pass")
+    # both again over the packed group table: the same bits
+    groups = zs.zero_chunk_groups(chunks, 2048)
+    gkw = dict(groups_dev=torch.from_numpy(groups.astype(np.int64)).to(DEV), n_groups=groups.size - 1)
+    gw, gm, gv = to_dev(w, F32), to_dev(m, F32), to_dev(v, F32)
+    gp = torch.zeros_like(dp)
+    zs.zero_adam_step(chunks_dev=dch, n_chunks=chunks.size, begin=begin, end=end, master=gw, exp_avg=gm,
+                      exp_avg_sq=gv, local_base=lb, step=4, rank_grads=dgr, divisor=float(R), param16=gp,
+                      **gkw, **HP)
+    rw, rm, rv = to_dev(w, F32), to_dev(m, F32), to_dev(v, F32)
+    zs.zero_adam_step(chunks_dev=dch, n_chunks=chunks.size, begin=begin, end=end, master=rw, exp_avg=rm,
+                      exp_avg_sq=rv, local_base=lb, step=4, reduced_g=g_dev, **gkw, **HP)
+    for a, c, x in ((dw, gw, rw), (dm, gm, rm), (dv, gv, rv)):
+        assert_bits_equal(from_dev(c), from_dev(a), what + " grouped fused")
+        assert_bits_equal(from_dev(x), from_dev(a), what + " grouped two-pass")
+    assert np.array_equal(from_dev(gp), from_dev(dp)), what + " grouped p16"
+
+
 def test_no_op_cases_leave_memory_untouched():
     dw = torch.full((16,), 3.0, device=DEV)
     dm, dv = torch.zeros(16, device=DEV), torch.zeros(16, device=DEV)
