@@ -1,0 +1,97 @@
+"""Seeded random layouts through the fused step, against the oracle.
+
+Each case draws a tensor list (sizes from 1 to a few thousand, some of them
+multiples of the alignment so that runs merge across tensors), a rank count,
+an alignment, a chunk size, an owner, gradient and write-back dtypes,
+Adam or AdamW, a clip factor, and whether the packed group table is used.
+Master weights and moments: |gpu - oracle| <= 1e-7 + 1e-6 |oracle|; the
+16-bit copy within 1 ulp of the oracle's rounding, with padding and other
+owners' elements untouched.
+"""
+import random
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import BF16, F16, F32, assert_p16_within_ulp, assert_state_close, from_dev, gen, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import zero_sharded_optimizer_owned_amd as zs  # noqa: E402
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    zs.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _case(seed):
+    rnd = random.Random(seed)
+    A = rnd.choice([1, 8, 64])
+    sizes = []
+    for _ in range(rnd.randrange(1, 40)):
+        kind = rnd.random()
+        if kind < 0.3:
+            sizes.append(A * rnd.randrange(1, 40))      # no padding: merges with its neighbours
+        elif kind < 0.6:
+            sizes.append(rnd.randrange(1, 20))          # shorter than a vector
+        else:
+            sizes.append(rnd.randrange(1, 3000))
+    R = rnd.choice([1, 2, 3, 4, 5, 8, 11, 16, 19])
+    gcode = rnd.choice([F16, BF16, F32])
+    pcode = rnd.choice([F16, BF16, 0])
+    return dict(sizes=sizes, A=A, R=R, owner=rnd.randrange(R), C=rnd.choice([8, 64, 256, 2048]),
+                gcode=gcode, pcode=pcode, adamw=rnd.random() < 0.7, wd=rnd.choice([0.0, 1e-2]),
+                clip=rnd.choice([1.0, 0.25]), grouped=rnd.random() < 0.5, step=rnd.randrange(1, 50))
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_layout_step_matches_oracle(seed):
+    c = _case(seed)
+    print(f"case {seed}: {c}", flush=True)
+    numels, R = c["sizes"], c["R"]
+    off, total, b, e = zs.zero_shard_layout(numels, R, c["A"])
+    begin, end = int(b[c["owner"]]), int(e[c["owner"]])
+    lb = begin & ~7
+    size = max(8, end - lb)
+    grads = [gen(seed, synth.STREAM_GRAD, total, synth.DIST_NORMAL, 1e-3, c["gcode"], rank=r) for r in range(R)]
+    w = gen(seed, synth.STREAM_MASTER, size, synth.DIST_NORMAL, 0.02, F32)
+    m = gen(seed, synth.STREAM_EXP_AVG, size, synth.DIST_NORMAL, 5e-4, F32)
+    v = gen(seed, synth.STREAM_EXP_AVG_SQ, size, synth.DIST_SQUARE, 1e-4, F32)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=c["wd"], adamw=c["adamw"])
+    chunks = zs.zero_chunk_table(numels, off, begin, end, c["C"])
+    kw = {}
+    if c["grouped"] and chunks.size:
+        groups = zs.zero_chunk_groups(chunks, c["C"])
+        kw = dict(groups_dev=torch.from_numpy(groups.astype(np.int64)).to(DEV), n_groups=groups.size - 1)
+    dw, dm, dv = to_dev(w, F32), to_dev(m, F32), to_dev(v, F32)
+    sentinel = 0x7BFF if c["pcode"] == F16 else 0x3F80
+    p_host = np.full(total + 8, sentinel, dtype=np.uint16)
+    dp = to_dev(p_host, c["pcode"]) if c["pcode"] else None
+    zs.zero_adam_step(chunks_dev=zs.chunks_to_device(chunks) if chunks.size else None, n_chunks=chunks.size,
+                      begin=begin, end=end, master=dw, exp_avg=dm, exp_avg_sq=dv, local_base=lb,
+                      step=c["step"], rank_grads=[to_dev(g, c["gcode"]) for g in grads], divisor=float(R),
+                      param16=dp, clip_coef=c["clip"], **kw, **hp)
+    ranges = oracle.real_ranges(numels, list(off), begin, end)
+    oracle.owner_step(ranges, oracle.hyper(step=c["step"], clip_coef=c["clip"], **hp), w, m, v, lb,
+                      grads=grads, gdtype=c["gcode"], divisor=float(R),
+                      p16=p_host if c["pcode"] else None, pdtype=c["pcode"])
+    assert_state_close(from_dev(dw), w, f"case {seed} w")
+    assert_state_close(from_dev(dm), m, f"case {seed} m")
+    assert_state_close(from_dev(dv), v, f"case {seed} v")
+    if c["pcode"]:
+        got = from_dev(dp)
+        real = np.zeros(total + 8, dtype=bool)
+        for s, t in ranges:
+            real[s:t] = True
+        assert np.all(got[~real] == sentinel), f"case {seed}: padding or foreign elements written"
+        assert_p16_within_ulp(got[real], p_host[real], f"case {seed} p16")
