@@ -95,3 +95,51 @@ def test_random_layout_step_matches_oracle(seed):
             real[s:t] = True
         assert np.all(got[~real] == sentinel), f"case {seed}: padding or foreign elements written"
         assert_p16_within_ulp(got[real], p_host[real], f"case {seed} p16")
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_flat_reduce_matches_oracle(seed):
+    """The flat rank reduce with random rank count, dtype, range ends, buffer
+    bases, divisor, accumulation mode and fused check: bit-exact, flag exact,
+    squared norm 1e-9 relative.  Elements outside the range stay untouched."""
+    from helpers import assert_bits_equal
+
+    rnd = random.Random(1000 + seed)
+    R = rnd.choice([1, 2, 3, 4, 7, 8, 9, 16, 17, 31, 32, 33, 64])
+    code = rnd.choice([F16, BF16, F32])
+    begin = rnd.randrange(0, 80)
+    n = rnd.choice([0, 1, 7, 9, rnd.randrange(10, 3000), rnd.randrange(3000, 70_000)])
+    end = begin + n
+    grad_base = rnd.choice([0, begin & ~7])
+    out_base = rnd.choice([0, begin & ~7])
+    divisor = rnd.choice([float(R), float(R) * 65536.0, 3.0, 0.75])
+    mode = rnd.choice([0, 1, 2])
+    check = rnd.random() < 0.5
+    print(f"case {seed}: R={R} code={code} begin={begin} n={n} grad_base={grad_base} out_base={out_base} "
+          f"divisor={divisor} mode={mode} check={check}", flush=True)
+    total = end + 8
+    grads = [gen(2000 + seed, synth.STREAM_GRAD, total, synth.DIST_NORMAL, 1e-2, code, rank=r) for r in range(R)]
+    start = gen(2000 + seed, synth.STREAM_EXP_AVG, total - out_base, synth.DIST_NORMAL, 1e-2, F32)
+    out = to_dev(start.copy(), F32)
+    kw = {}
+    if check:
+        ws = zs.check_workspace(max(n, 1), DEV)
+        ov = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+        ss = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+        kw = dict(check=(ov, ss, ws))
+    zs.zero_reduce_owned([to_dev(g[grad_base:], code) for g in grads], begin, n, divisor, out,
+                         grad_base=grad_base, out_base=out_base, accumulate=mode, **kw)
+    want = start.copy()
+    if n:
+        seg = [g[begin:end] for g in grads]
+        dst = want[begin - out_base:end - out_base]
+        if mode == 2:
+            oracle.reduce_add(seg, code, divisor, dst)
+        else:
+            dst[:] = oracle.reduce(seg, code, divisor, out=dst.copy(), accumulate=mode == 1)
+    assert_bits_equal(from_dev(out), want, f"case {seed}")
+    if check and n:
+        flag, sumsq = oracle.grad_check(want[begin - out_base:end - out_base])
+        assert int(ov.item()) == flag
+        if not flag:
+            assert abs(ss.item() - sumsq) <= 1e-9 * sumsq
