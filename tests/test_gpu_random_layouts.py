@@ -1,4 +1,7 @@
-"""Seeded random layouts through the fused step, against the oracle.
+"""Seeded random cases against the oracle: the fused step, the flat reduce, the
+fp32 export/import and the ZeRO-3 partition and gather copies.
+
+Fused step:
 
 Each case draws a tensor list (sizes from 1 to a few thousand, some of them
 multiples of the alignment so that runs merge across tensors), a rank count,
@@ -143,3 +146,89 @@ def test_random_flat_reduce_matches_oracle(seed):
         assert int(ov.item()) == flag
         if not flag:
             assert abs(ss.item() - sumsq) <= 1e-9 * sumsq
+
+
+def _random_sizes(rnd, A):
+    out = []
+    for _ in range(rnd.randrange(1, 60)):
+        k = rnd.random()
+        out.append(A * rnd.randrange(1, 30) if k < 0.3 else rnd.randrange(1, 40) if k < 0.6
+                   else rnd.randrange(1, 5000))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_export_import_matches_oracle(seed):
+    """Owner shards to dense per-tensor fp32 and back, every owner, with and
+    without chunk groups: bit-exact against the oracle's consolidation."""
+    from helpers import assert_bits_equal
+
+    rnd = random.Random(3000 + seed)
+    A = rnd.choice([1, 8, 64])
+    numels = _random_sizes(rnd, A)
+    R = rnd.choice([1, 2, 3, 5, 8, 13])
+    C = rnd.choice([8, 64, 512, 2048])
+    grouped = rnd.random() < 0.5
+    print(f"case {seed}: {len(numels)} tensors R={R} A={A} C={C} grouped={grouped}", flush=True)
+    shards = [zs.OwnerShard(numels, R, r, align=A, max_chunk=C, device=DEV) for r in range(R)]
+    if not grouped:
+        for sh in shards:
+            sh.groups_dev = None
+    arrays = [gen(3000 + seed, synth.STREAM_MASTER, max(8, sh.local_size), synth.DIST_NORMAL, 0.02, F32, rank=r)
+              for r, sh in enumerate(shards)]
+    dense = torch.full((sum(numels),), float("nan"), device=DEV)
+    for sh, a in zip(shards, arrays):
+        sh.to_dense(to_dev(a, F32), dense)
+    owners = [(sh.begin, sh.end) for sh in shards]
+    want = oracle.consolidate(numels, list(shards[0].offsets), owners, arrays, [sh.local_base for sh in shards])
+    assert_bits_equal(from_dev(dense), want, f"case {seed} export")
+    for sh in shards:
+        back = torch.full((max(8, sh.local_size),), -1.0, device=DEV)
+        sh.from_dense(dense, back)
+        ref = oracle.distribute(numels, list(sh.offsets), sh.begin, sh.end, want,
+                                np.full(max(8, sh.local_size), -1.0, dtype=np.float32), sh.local_base)
+        assert_bits_equal(from_dev(back), ref, f"case {seed} import")
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_stage3_partition_and_gather_match_oracle(seed):
+    """ZeRO-3 per-tensor shards and gathers of random live sets, with random span
+    limits and with and without span groups: bit-exact against the oracle."""
+    from helpers import assert_bits_equal
+
+    rnd = random.Random(4000 + seed)
+    code = rnd.choice([BF16, F32])
+    sizes = _random_sizes(rnd, 8)
+    R = rnd.choice([1, 2, 3, 4, 8, 16])
+    max_span = rnd.choice([1, 7, 64, 4096])
+    grouped = rnd.random() < 0.5
+    print(f"case {seed}: {len(sizes)} tensors R={R} code={code} max_span={max_span} grouped={grouped}",
+          flush=True)
+    dense = gen(4000 + seed, synth.STREAM_MASTER, sum(sizes), synth.DIST_NORMAL, 0.02, code)
+    dense_dev = to_dev(dense, code)
+    _, resident, _ = zs.zero3_storage(sizes, R)
+    want_shards = oracle.stage3_shards(sizes, R, dense)
+    eb = 2 if code == BF16 else 4
+
+    def gk(spans):
+        if not grouped or not spans.size:
+            return {}
+        g = zs.zero_span_groups(spans, eb)
+        return dict(groups_dev=torch.from_numpy(g.astype(np.int64)).to(DEV), n_groups=g.size - 1)
+
+    shard_devs = []
+    for r in range(R):
+        spans = zs.zero3_partition_spans(sizes, R, r, max_span=max_span)
+        buf = torch.zeros(resident, dtype=dense_dev.dtype, device=DEV)
+        zs.zero_copy_spans(zs.spans_to_device(spans) if spans.size else None, spans.size, [dense_dev], buf,
+                           **gk(spans))
+        assert_bits_equal(from_dev(buf), want_shards[r], f"case {seed} shard {r}")
+        shard_devs.append(buf)
+    for _ in range(3):
+        live = rnd.sample(range(len(sizes)), rnd.randrange(1, len(sizes) + 1))
+        _, _, gathered = zs.zero3_storage(sizes, R, live)
+        spans = zs.zero3_gather_spans(sizes, R, live, max_span=max_span)
+        out = torch.full((gathered,), 7, dtype=dense_dev.dtype, device=DEV)
+        zs.zero_copy_spans(zs.spans_to_device(spans), spans.size, shard_devs, out, **gk(spans))
+        assert_bits_equal(from_dev(out), oracle.stage3_gather(sizes, R, want_shards, live),
+                          f"case {seed} gather {live}")
