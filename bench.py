@@ -225,10 +225,8 @@ class Workload:
         # where only the owner's slice is held (ZeRO-3 style), param_base = lb
         if cfg == 4:
             self.p16, self.param_base = torch.zeros(end - lb, dtype=pdt, device=dev), lb
-            self.g32 = torch.empty(end - lb, dtype=torch.float32, device=dev)
-            self.ov = torch.zeros(1, dtype=torch.int32, device=dev)
-            self.ss = torch.zeros(1, dtype=torch.float64, device=dev)
-            self.ws = zs.check_workspace(end - sh.begin, dev)
+            # owner-local fp32 gradient, flag, norm and check workspace of the two-pass step
+            self.g32, self.ov, self.ss, self.ws = sh.check_buffers()
             self.divisor = float(R) * 65536.0
         else:
             self.p16 = torch.zeros(sh.padded_total, dtype=pdt, device=dev)
@@ -371,23 +369,16 @@ class Workload:
                 saved = (self.grads[5][12345].clone(), self.grads[17][777_777].clone())
                 self.grads[5][12345] = float("inf")
                 self.grads[17][777_777] = float("nan")
-            if timing is not None:
-                timing[0].record()
-            zs.zero_reduce_owned(self.grads, sh.begin, sh.end - sh.begin, self.divisor, self.g32,
-                                 grad_base=sh.local_base, out_base=sh.local_base,
-                                 check=(self.ov, self.ss, self.ws))
-            if timing is not None:
-                timing[1].record()
-            flag, sumsq = int(self.ov.item()), float(self.ss.item())  # 12 bytes to the host
+            # reduce + check, 16 bytes to the host, then AdamW from g unless overflowed
+            updated, _ = sh.checked_step(step=self.t, hyper=HP, rank_grads=self.grads, grad_base=sh.local_base,
+                                         divisor=self.divisor, max_norm=1.0, param16=self.p16,
+                                         param_base=self.param_base, grid_blocks=self.grid, events=timing)
             if inject:
                 self.grads[5][12345] = saved[0]
                 self.grads[17][777_777] = saved[1]
-            if flag:
+            if not updated:
                 self.skipped += 1
                 return True
-            coef = zs.zero_clip_coef(sumsq, 1.0, 1e-6)
-            sh.adam_step(step=self.t, hyper=HP, reduced_g=self.g32, param16=self.p16,
-                         param_base=self.param_base, clip_coef=coef, grid_blocks=self.grid)
             self.t += 1
             return False
         if timing is not None:

@@ -403,6 +403,54 @@ def test_fused_step_every_rank_path(code, R):
     assert np.array_equal(from_dev(gp), from_dev(dp)), what + " grouped p16"
 
 
+def test_checked_step_skips_clips_and_updates():
+    """OwnerShard.checked_step: reduce + check, the host decision, AdamW from the
+    reduced gradient with the clip factor; an overflowed step writes no state;
+    an empty owner launches nothing."""
+    numels, R, A = [3000, 77, 20_001, 5], 4, 64
+    sh = zs.OwnerShard(numels, R, 1, align=A, max_chunk=512, device=DEV)
+    sh.alloc_state()
+    lb, begin, end, total = sh.local_base, sh.begin, sh.end, sh.padded_total
+    grads = _rank_inputs(F16, R, total, seed=23, scale=0.5)  # a norm far above 1: the clip applies
+    dgr = [to_dev(g, F16) for g in grads]
+    w = gen(23, synth.STREAM_MASTER, sh.local_size, synth.DIST_NORMAL, 0.02, F32)
+    m = gen(23, synth.STREAM_EXP_AVG, sh.local_size, synth.DIST_NORMAL, 5e-4, F32)
+    v = gen(23, synth.STREAM_EXP_AVG_SQ, sh.local_size, synth.DIST_SQUARE, 1e-4, F32)
+    for dst, src in ((sh.master, w), (sh.exp_avg, m), (sh.exp_avg_sq, v)):
+        dst[:src.size].copy_(to_dev(src, F32))
+    dp = torch.zeros(total, dtype=torch.float16, device=DEV)
+    updated, coef = sh.checked_step(step=3, hyper=HP, rank_grads=dgr, divisor=float(R), param16=dp)
+    assert updated
+    g_or = oracle.reduce([g[begin:end] for g in grads], F16, float(R))
+    flag, sumsq = oracle.grad_check(g_or)
+    assert flag == 0
+    want_coef = oracle.clip_coef(sumsq)
+    assert want_coef < 0.5 and abs(coef - want_coef) <= 1e-6 * want_coef
+    g_loc = np.zeros(sh.local_size, dtype=np.float32)
+    g_loc[begin - lb:] = g_or
+    ranges = oracle.real_ranges(numels, list(sh.offsets), begin, end)
+    ow, om, ov_ = w.copy(), m.copy(), v.copy()
+    p_or = np.zeros(total, dtype=np.uint16)
+    oracle.owner_step(ranges, oracle.hyper(step=3, clip_coef=coef, **HP), ow, om, ov_, lb, reduced_g=g_loc,
+                      p16=p_or, pdtype=F16)
+    assert_state_close(from_dev(sh.master)[:sh.local_size], ow, "w")
+    assert_state_close(from_dev(sh.exp_avg)[:sh.local_size], om, "m")
+    assert_state_close(from_dev(sh.exp_avg_sq)[:sh.local_size], ov_, "v")
+    assert_p16_within_ulp(from_dev(dp), p_or, "p16")
+    # an inf in one rank: the step is skipped and no state or 16-bit value changes
+    before = [from_dev(x).copy() for x in (sh.master, sh.exp_avg, sh.exp_avg_sq, dp)]
+    dgr[2][begin + 5] = float("inf")
+    assert sh.checked_step(step=4, hyper=HP, rank_grads=dgr, divisor=float(R), param16=dp) == (False, None)
+    for a, b in zip(before, (sh.master, sh.exp_avg, sh.exp_avg_sq, dp)):
+        assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              from_dev(b).view(np.uint32) if a.dtype == np.float32 else from_dev(b))
+    # an empty owner: nothing to do
+    empty = zs.OwnerShard([3, 2], 9, 0, align=1, device=DEV)
+    assert empty.begin == empty.end
+    empty.alloc_state()
+    assert empty.checked_step(step=1, hyper=HP, rank_grads=[to_dev(np.zeros(8, np.float32), F32)]) == (True, 1.0)
+
+
 def test_no_op_cases_leave_memory_untouched():
     dw = torch.full((16,), 3.0, device=DEV)
     dm, dv = torch.zeros(16, device=DEV), torch.zeros(16, device=DEV)

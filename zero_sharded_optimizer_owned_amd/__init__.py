@@ -551,6 +551,52 @@ class OwnerShard:
                        **self._group_args(),
                        clip_coef=clip_coef, grid_blocks=grid_blocks, **hyper)
 
+    def check_buffers(self):
+        """(owner-local fp32 gradient, overflow flag int32[1], squared norm
+        float64[1], check workspace) used by ``checked_step``, allocated on first
+        use and kept.  The flag and the norm share one 16-byte buffer, so one
+        copy brings both to the host."""
+        torch = _torch()
+        if getattr(self, "_check_bufs", None) is None:
+            g = torch.zeros(max(8, self.local_size), dtype=torch.float32, device=self.device)
+            flag_norm = torch.zeros(16, dtype=torch.uint8, device=self.device)
+            ws = check_workspace(max(1, self.end - self.begin), self.device)
+            self._flag_norm = flag_norm
+            self._check_bufs = (g, flag_norm[0:4].view(torch.int32), flag_norm[8:16].view(torch.float64), ws)
+        return self._check_bufs
+
+    def checked_step(self, *, step: int, hyper: dict, rank_grads, grad_base: int = 0, divisor: float = 1.0,
+                     max_norm: float = 1.0, param16=None, param_base: int = 0, grid_blocks: int = 0,
+                     events=None):
+        """The two-pass step with an overflow skip and a norm clip: the rank reduce
+        with the fused check into the owner-local fp32 gradient, one 16-byte copy
+        of (overflow flag, squared norm) to the host, then -- unless the reduced
+        gradient holds a non-finite value -- AdamW from it scaled by
+        ``min(1, max_norm / (sqrt(sumsq) + 1e-6))``.
+
+        Returns ``(updated, clip_coef)``; ``updated`` is False for a skipped step
+        (nothing but the gradient buffer was written), and the caller advances
+        its step count only when it is True.  An empty owner returns (True, 1.0)
+        without a launch.  ``divisor`` folds in a static loss scale.  ``events``:
+        optional (start, end) CUDA events recorded around the reduce launch.
+        """
+        if self.end == self.begin:  # an empty owner: nothing to reduce or update
+            return True, 1.0
+        g, ov, ss, ws = self.check_buffers()
+        if events is not None:
+            events[0].record()
+        zero_reduce_owned(rank_grads, self.begin, self.end - self.begin, divisor, g,
+                          grad_base=grad_base, out_base=self.local_base, check=(ov, ss, ws))
+        if events is not None:
+            events[1].record()
+        host = self._flag_norm.cpu().numpy()  # waits for the reduce
+        if int(host[0:4].view(np.int32)[0]):
+            return False, None
+        coef = zero_clip_coef(float(host[8:16].view(np.float64)[0]), max_norm)
+        self.adam_step(step=step, hyper=hyper, reduced_g=g, param16=param16, param_base=param_base,
+                       clip_coef=coef, grid_blocks=grid_blocks)
+        return True, coef
+
     # -- export / import of fp32 shard data in the dense per-tensor layout
     def to_dense(self, owner_array, dense) -> None:
         """Write this owner's real elements of an owner-local fp32 array into dense weights."""
