@@ -98,7 +98,9 @@ PROBE_MIX = {"adam_step_f16_f16": (10, 7), "adam_step_bf16_bf16": (2, 1), "reduc
 def probe_gbps(n_src: int, n_dst: int, total_bytes: float = 8e9, launches: int = 5, reps: int = 3) -> float:
     """HBM GB/s of the library's streaming probe for an n_src:n_dst mix of
     equal streams, about `total_bytes` moved per launch (far above the caches):
-    the best of `reps` timings of `launches` launches after five warm-up ones."""
+    the best of `reps` timings of `launches` launches after five warm-up ones,
+    in either piece order (round-robin over the XCDs or XCD-contiguous runs;
+    few streams go faster in contiguous runs, many in round-robin)."""
     import torch
 
     import zero_sharded_optimizer_owned_amd as zs
@@ -106,18 +108,19 @@ def probe_gbps(n_src: int, n_dst: int, total_bytes: float = 8e9, launches: int =
     per = int(total_bytes // (n_src + n_dst)) // (1 << 20) * (1 << 20)
     srcs = [torch.zeros(per, dtype=torch.uint8, device="cuda") for _ in range(n_src)]
     dsts = [torch.empty(per, dtype=torch.uint8, device="cuda") for _ in range(n_dst)]
-    for _ in range(5):
-        zs.zero_stream_probe(srcs, dsts)
     best = float("inf")
-    for _ in range(reps):
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        s.record()
-        for _ in range(launches):
-            zs.zero_stream_probe(srcs, dsts)
-        e.record()
-        torch.cuda.synchronize()
-        best = min(best, s.elapsed_time(e) / launches)
+    for order in (0, 1):
+        for _ in range(5):
+            zs.zero_stream_probe(srcs, dsts, order)
+        for _ in range(reps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            s.record()
+            for _ in range(launches):
+                zs.zero_stream_probe(srcs, dsts, order)
+            e.record()
+            torch.cuda.synchronize()
+            best = min(best, s.elapsed_time(e) / launches)
     del srcs, dsts
     torch.cuda.empty_cache()
     return (n_src + n_dst) * per / (best / 1e3) / 1e9

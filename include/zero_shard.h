@@ -453,13 +453,17 @@ int zero_copy_spans(const zero_copy_span *spans, uint64_t n_spans, const void *c
  *                           aligned; n_src, n_dst <= ZERO_MAX_PROBE_STREAMS,
  *                           not both 0 (an empty array may be NULL)
  * bytes                     bytes per stream, a multiple of 16 (0: no launch)
+ * order                     0: block b takes piece b (blocks are dealt to the
+ *                           8 XCDs in turn); 1: each XCD takes one contiguous
+ *                           run of pieces.  Which is faster depends on the
+ *                           number of streams.
  * A destination that overlaps a source or another destination gives
  * unspecified contents (no fault: every access stays inside the streams).
  * Errors: EINVAL (stream counts, NULL or misaligned pointers, bytes not a
- * multiple of 16); EHIP.
+ * multiple of 16, order not 0 or 1); EHIP.
  * -------------------------------------------------------------------------- */
 int zero_stream_probe(const void *const *srcs, uint32_t n_src, void *const *dsts, uint32_t n_dst,
-                      uint64_t bytes, hipStream_t stream);
+                      uint64_t bytes, int order, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -199,15 +199,16 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
         assert b"workspace" in L.zero_last_error()
     # bandwidth probe: stream counts, byte size, NULL and misaligned pointers
     two = (ct.c_void_p * 2)(0x1000, 0x2000)
-    assert L.zero_stream_probe(two, 0, two, 0, 64, None) == zs.ZERO_EINVAL
-    assert L.zero_stream_probe(two, 65, two, 1, 64, None) == zs.ZERO_EINVAL
-    assert L.zero_stream_probe(two, 1, two, 65, 64, None) == zs.ZERO_EINVAL
-    assert L.zero_stream_probe(two, 1, two, 1, 24, None) == zs.ZERO_EINVAL
-    assert L.zero_stream_probe(None, 1, two, 1, 64, None) == zs.ZERO_EINVAL
-    assert L.zero_stream_probe(two, 1, None, 1, 64, None) == zs.ZERO_EINVAL
-    assert L.zero_stream_probe(bad, 1, two, 1, 64, None) == zs.ZERO_EINVAL
-    assert L.zero_stream_probe((ct.c_void_p * 1)(0), 1, two, 1, 64, None) == zs.ZERO_EINVAL
-    assert L.zero_stream_probe(two, 1, two, 1, 0, None) == zs.ZERO_OK  # nothing to move
+    assert L.zero_stream_probe(two, 0, two, 0, 64, 0, None) == zs.ZERO_EINVAL
+    assert L.zero_stream_probe(two, 65, two, 1, 64, 0, None) == zs.ZERO_EINVAL
+    assert L.zero_stream_probe(two, 1, two, 65, 64, 0, None) == zs.ZERO_EINVAL
+    assert L.zero_stream_probe(two, 1, two, 1, 24, 0, None) == zs.ZERO_EINVAL
+    assert L.zero_stream_probe(None, 1, two, 1, 64, 0, None) == zs.ZERO_EINVAL
+    assert L.zero_stream_probe(two, 1, None, 1, 64, 0, None) == zs.ZERO_EINVAL
+    assert L.zero_stream_probe(bad, 1, two, 1, 64, 0, None) == zs.ZERO_EINVAL
+    assert L.zero_stream_probe((ct.c_void_p * 1)(0), 1, two, 1, 64, 0, None) == zs.ZERO_EINVAL
+    assert L.zero_stream_probe(two, 1, two, 1, 0, 0, None) == zs.ZERO_OK  # nothing to move
+    assert L.zero_stream_probe(two, 1, two, 1, 64, 2, None) == zs.ZERO_EINVAL  # order 0 or 1
 
 
 def test_check_workspace_grows_with_the_block_count():

@@ -21,13 +21,14 @@ def _gpu():
 
 @pytest.mark.parametrize("n_src,n_dst,n_vec", [(1, 1, 1), (1, 1, 64 * 4 * 3 + 5), (3, 2, 100_003),
                                                (10, 7, 70_001), (33, 1, 9_999), (64, 64, 517)])
-def test_probe_writes_xor_of_sources(n_src, n_dst, n_vec):
+@pytest.mark.parametrize("order", [0, 1])
+def test_probe_writes_xor_of_sources(n_src, n_dst, n_vec, order):
     rng = np.random.default_rng(n_src * 1000 + n_vec)
     host = [rng.integers(0, 2 ** 32, size=4 * n_vec, dtype=np.uint32) for _ in range(n_src)]
     srcs = [torch.from_numpy(h.view(np.int32)).to("cuda") for h in host]
     dsts = [torch.full((4 * n_vec + 8,), -7, dtype=torch.int32, device="cuda") for _ in range(n_dst)]
     views = [d[:4 * n_vec] for d in dsts]
-    zs.zero_stream_probe(srcs, views)
+    zs.zero_stream_probe(srcs, views, order)
     torch.cuda.synchronize()
     want = np.bitwise_xor.reduce(np.stack(host), axis=0) if n_src > 1 else host[0]
     for d in dsts:

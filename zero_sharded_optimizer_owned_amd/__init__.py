@@ -90,7 +90,7 @@ def load(path: str):
     L.zero3_partition_spans.argtypes = [P, U32, U32, U32, U32, P, U64, P]
     L.zero_copy_spans.argtypes = [P, U64, P, P, U32, P, U64, U32, P, U64, P]
     L.zero_span_groups.argtypes = [P, U64, U32, U32, P, U64, P]
-    L.zero_stream_probe.argtypes = [P, U32, P, U32, U64, P]
+    L.zero_stream_probe.argtypes = [P, U32, P, U32, U64, I, P]
     L.zero_check_workspace_bytes.argtypes = [U64, P]
     L.zero_chunk_groups.argtypes = [P, U64, U32, P, U64, P]
     return L
@@ -474,12 +474,13 @@ def zero_copy_spans(spans_dev, n_spans: int, srcs, dst, groups_dev=None, n_group
                                  dst.numel(), dst.element_size(), gptr, ng, _stream()))
 
 
-def zero_stream_probe(srcs, dsts) -> None:
+def zero_stream_probe(srcs, dsts, order: int = 0) -> None:
     """Bandwidth probe: every destination gets the bytewise XOR of all sources.
 
     All tensors are contiguous device tensors of one byte size (a multiple of
     16); one launch moves (len(srcs) + len(dsts)) * that many bytes.  No
-    destinations: reads only; no sources: writes zeros.
+    destinations: reads only; no sources: writes zeros.  ``order`` 0 deals the
+    pieces to the XCDs in turn, 1 gives each XCD one contiguous run.
     """
     if len(srcs) > ZERO_MAX_PROBE_STREAMS or len(dsts) > ZERO_MAX_PROBE_STREAMS or not (srcs or dsts):
         raise ValueError(f"at most {ZERO_MAX_PROBE_STREAMS} sources and destinations, not none of both")
@@ -492,7 +493,7 @@ def zero_stream_probe(srcs, dsts) -> None:
             if t.numel() * t.element_size() != nbytes:
                 raise ValueError("all probe streams must have the same byte size")
             arr[i] = t.data_ptr()
-    _check(lib().zero_stream_probe(sa, len(srcs), da, len(dsts), nbytes, _stream()))
+    _check(lib().zero_stream_probe(sa, len(srcs), da, len(dsts), nbytes, int(order), _stream()))
 
 
 # ---------------------------------------------------------------- convenience

@@ -30,6 +30,19 @@ int launch_status(const char* who);
 constexpr uint32_t kMaxChunkGrid = 1u << 23;
 uint32_t chunk_grid(uint64_t n_pieces, uint32_t requested);
 
+// The dispatcher deals a launch's blocks to the chip's 8 XCDs in turn (block b
+// to XCD b mod 8), so neighbouring pieces run on different XCDs at the same
+// time.  xcd_contiguous maps block b of a G-block grid to a piece index such
+// that each XCD takes one contiguous run of about G/8 pieces instead (a
+// bijection of [0, G)).  Measured with the streaming probe: contiguous runs
+// stream one source 6% faster and a 1:1 copy 2.4% faster, but lose 1-2% from
+// about ten streams on; kernels opt in where their own A/B says so.
+constexpr uint64_t kXcds = 8;
+__device__ __forceinline__ uint64_t xcd_contiguous(uint64_t b, uint64_t G) {
+  const uint64_t x = b % kXcds, k = b / kXcds, q = G / kXcds, r = G % kXcds;
+  return x * q + (x < r ? x : r) + k;
+}
+
 // Dynamic LDS bytes that let at most `per_cu` blocks of a kernel reside on one
 // CU at a time, for a kernel whose own arrays take `static_bytes` of LDS (the
 // reservation only caps residency; nothing reads it).  0 -- no cap -- when

@@ -328,6 +328,7 @@ struct ReduceArgs {
   RankSet rs;
   uint64_t begin, end;
   uint64_t piece;  // vectors per block piece, a multiple of kBlock
+  int xcd_order;   // pieces in XCD-contiguous runs (xcd_contiguous) rather than dealt round-robin
   float* out;
   uint64_t out_base;
   CheckOut chk;
@@ -366,8 +367,9 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs a) {
     }
   }
   const uint64_t v0 = a0 / 8, n_vec = a1 / 8 - v0;
+  const uint64_t blk = a.xcd_order ? xcd_contiguous(blockIdx.x, gridDim.x) : blockIdx.x;
   const uint64_t stride = (uint64_t)gridDim.x * a.piece;
-  for (uint64_t p0 = (uint64_t)blockIdx.x * a.piece; p0 < n_vec; p0 += stride) {
+  for (uint64_t p0 = blk * a.piece; p0 < n_vec; p0 += stride) {
     const uint64_t p1 = min(n_vec, p0 + a.piece);
     for (uint64_t v = p0 + threadIdx.x; v < p1; v += kBlock) {
       const uint64_t f[1] = {(v0 + v) * 8};
@@ -393,9 +395,9 @@ __global__ void __launch_bounds__(kBlock) reduce_kernel(const ReduceArgs a) {
   }
   if (CHECK) {
     block_reduce(sq, bad);
-    if (threadIdx.x == 0) {
-      a.chk.partial[blockIdx.x] = sq;
-      a.chk.flags[blockIdx.x] = bad;
+    if (threadIdx.x == 0) {  // indexed by piece, so the fold's tree is the same in either order
+      a.chk.partial[blk] = sq;
+      a.chk.flags[blk] = bad;
     }
   }
 }
@@ -883,6 +885,10 @@ extern "C" int zero_reduce_owned(const void* const* rank_grads, uint32_t R, int 
   const uint64_t a0 = std::min<uint64_t>(a.end, (begin + 7) & ~7ull);
   const uint64_t a1 = std::max<uint64_t>(a0, a.end & ~7ull);
   a.piece = reduce_piece(R);
+  // One source (the microstep accumulation): XCD-contiguous runs of pieces,
+  // measured +7.7% for a bf16 source added into fp32; from 16 sources on the
+  // round-robin order is faster (-3.8% and -0.9% for 16 and 64 ranks).
+  a.xcd_order = R == 1 ? 1 : 0;
   const uint32_t grid = flat_grid(a1 / 8 - a0 / 8, a.piece);
   if (check) a.chk = check_layout(workspace, grid);
   switch (grad_dtype) {
