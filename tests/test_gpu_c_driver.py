@@ -44,7 +44,7 @@ def test_c_driver_is_built_and_checks_its_arguments():
 @pytest.mark.parametrize("gcode,pcode,R,owner", [(F16, F16, 4, 1), (BF16, BF16, 8, 5), (F32, BF16, 3, 2)])
 def test_c_driver_step_matches_oracle(tmp_path, gcode, pcode, R, owner):
     numels, align, step = [1000, 37, 5003, 1, 64, 777, 20_000], 64, 3
-    off, total, owners = oracle.layout(numels, R, align)  # sizes the files; the driver asks the library
+    off, total, owners = oracle.layout(numels, R, align)  # sizes the files; the C program asks the library
     begin, end = owners[owner]
     assert end > begin
     lb = begin & ~7

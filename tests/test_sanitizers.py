@@ -1,7 +1,7 @@
 """The oracle and the library's host code built with AddressSanitizer and
 UndefinedBehaviorSanitizer (gcc/g++, CPU only) and driven over random inputs
-by the drivers in tests/sanitize/: any out-of-bounds access, use after free or
-undefined operation aborts the driver."""
+by the test programs in tests/sanitize/: any out-of-bounds access, use after
+free or undefined operation aborts the program."""
 import os
 import shutil
 import subprocess
