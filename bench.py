@@ -420,26 +420,41 @@ def cpu_baseline(w: Workload, seconds: float):
     idx = synth.arange(lb, hi)
     gcode = {2: synth.F16, 3: synth.BF16, 4: synth.F16, 5: synth.F32}[cfg]
     scale = w.grad_scale if cfg != 5 else 1e-3
+    micro = None  # the per-step microstep work timed with the owner step (config 5)
     if w.schedule == "per-backward":
-        # the owner's accumulator: every microstep reduces the ranks' values (untimed)
+        # each of the eight microsteps reduces the 16 ranks' owned values into the owner's
+        # accumulator (timed below; the eight microsteps reuse one microstep's values)
+        rows = [synth.values(synth.stream_key(seed, synth.STREAM_MICRO, r, 0), synth.arange(lo, hi),
+                             synth.DIST_NORMAL, 1e-3, synth.BF16) for r in range(w.R)]
         acc = np.zeros(hi - lo, dtype=np.float32)
-        for k in range(8):
-            row = [synth.values(synth.stream_key(seed, synth.STREAM_MICRO, r, k), synth.arange(lo, hi),
-                                synth.DIST_NORMAL, 1e-3, synth.BF16) for r in range(w.R)]
-            if k == 0:
-                acc[:] = oracle.reduce(row, synth.BF16, float(w.R))
-            else:
-                oracle.reduce_add(row, synth.BF16, float(w.R), acc)
+
+        def micro():
+            acc[:] = oracle.reduce(rows, synth.BF16, float(w.R))
+            for _ in range(7):
+                oracle.reduce_add(rows, synth.BF16, float(w.R), acc)
         grads = None
     elif cfg == 5:
+        # the owner's 16 rank slices: each the eight-microstep accumulation of its rank
         grads = []
         for r in range(w.R):
-            acc = np.zeros(hi - lb, dtype=np.float32)
+            acc_r = np.zeros(hi - lb, dtype=np.float32)
             for k in range(8):
                 g = synth.values(synth.stream_key(seed, synth.STREAM_MICRO, r, k), idx, synth.DIST_NORMAL,
                                  1e-3, synth.BF16)
-                oracle.accumulate(g, synth.BF16, acc, first=(k == 0))
-            grads.append(acc)
+                oracle.accumulate(g, synth.BF16, acc_r, first=(k == 0))
+            grads.append(acc_r)
+        # the local rank's eight microsteps over its whole flat buffer, which is
+        # padded_total / owned elements per owned element (timed below; the eight
+        # microsteps reuse one microstep's values)
+        flat_per_owned = sh.padded_total / sh.n_real
+        m = int(round((hi - lb) * flat_per_owned))
+        gm = synth.values(synth.stream_key(seed, synth.STREAM_MICRO, sh.owner, 0), synth.arange(0, m),
+                          synth.DIST_NORMAL, 1e-3, synth.BF16)
+        acc_local = np.zeros(m, dtype=np.float32)
+
+        def micro():
+            for k in range(8):
+                oracle.accumulate(gm, synth.BF16, acc_local, first=(k == 0))
     else:
         grads = [synth.values(synth.stream_key(seed, synth.STREAM_GRAD, r), idx, synth.DIST_NORMAL,
                               scale, gcode) for r in range(w.R)]
@@ -454,6 +469,8 @@ def cpu_baseline(w: Workload, seconds: float):
     while True:
         wc, mc, vc = w0.copy(), m0.copy(), v0.copy()
         t_start = time.perf_counter()
+        if micro is not None:
+            micro()
         if w.schedule == "per-backward":
             gfull = np.zeros(hi - lb, dtype=np.float32)
             gfull[lo - lb:] = acc
@@ -476,11 +493,12 @@ def cpu_baseline(w: Workload, seconds: float):
         if el >= seconds or reps >= 1000:
             break
     if w.schedule == "per-backward":
-        what = "AdamW + cast from the owned accumulator; the eight per-microstep reduces untimed"
+        what = "eight reduce-and-adds of the 16 ranks' owned values, then AdamW + cast"
     elif cfg == 4:
         what = "reduce + check + clip + AdamW + cast"
     elif cfg == 5:
-        what = "reduce + AdamW + cast; the microstep accumulation untimed"
+        what = (f"eight microstep accumulations over {m} local flat elements "
+                f"({flat_per_owned:.1f} per owned element), then reduce + AdamW + cast")
     else:
         what = "reduce + AdamW + cast"
     return {"value": done / el, "unit": "params/s", "cores": oracle.num_threads(), "kind": "oracle",
