@@ -43,6 +43,15 @@ __device__ __forceinline__ uint64_t xcd_contiguous(uint64_t b, uint64_t G) {
   return x * q + (x < r ? x : r) + k;
 }
 
+// Between the two: the XCDs take runs of K consecutive pieces in turn (XCD x
+// gets pieces xK .. xK+K-1, then 8K + xK .. , and so on); a last partial
+// round keeps the plain order.  A bijection of [0, G); K = 1 is the identity.
+__device__ __forceinline__ uint64_t xcd_runs(uint64_t b, uint64_t G, uint64_t K) {
+  const uint64_t span = kXcds * K, full = G / span * span;
+  if (b >= full) return b;
+  return b / span * span + (b % kXcds) * K + (b / kXcds) % K;
+}
+
 // Dynamic LDS bytes that let at most `per_cu` blocks of a kernel reside on one
 // CU at a time, for a kernel whose own arrays take `static_bytes` of LDS (the
 // reservation only caps residency; nothing reads it).  0 -- no cap -- when

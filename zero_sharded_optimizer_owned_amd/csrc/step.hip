@@ -660,10 +660,14 @@ __device__ void adam_packed(const AdamArgs& a, uint64_t c0, uint64_t c1, uint32_
 // contiguous piece of every stream and exits; blocks are dispatched in chunk
 // order, which keeps the pieces in flight across the chip inside a narrow
 // window of each stream.  A grid smaller than the chunk count takes the
-// remaining chunks with a grid stride.
+// remaining chunks with a grid stride.  With rank gradients the XCDs take
+// runs of two consecutive chunks (xcd_runs): measured +7% for 8 bf16 ranks on
+// two boxes, within 0.6% for 4 fp16 or 16 fp32 ranks; from a stored gradient
+// the plain order is 2% faster, so it keeps that.
 template <int GDT, int PDT, int RC>
 __global__ void __launch_bounds__(kBlock) adam_kernel(const AdamArgs a) {
-  for (uint64_t c = blockIdx.x; c < a.n_chunks; c += gridDim.x)
+  constexpr uint64_t kRun = RC == kReduced ? 1 : 2;
+  for (uint64_t c = xcd_runs(blockIdx.x, gridDim.x, kRun); c < a.n_chunks; c += gridDim.x)
     adam_chunk<GDT, PDT, RC>(a, a.chunks[c], threadIdx.x);
 }
 
