@@ -6,12 +6,16 @@ import ctypes as ct
 import os
 import random
 import re
+import shutil
+import subprocess
 
 import numpy as np
 import pytest
 
 import oracle
 import zero_sharded_optimizer_owned_amd as zs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "zero_shard.h")
 
@@ -345,3 +349,18 @@ def test_span_groups_partition_the_table():
     cnt = np.zeros(1, dtype=np.uint64)
     assert zs.lib().zero_span_groups(None, 2, 2, 64, None, 0, cnt.ctypes.data) == zs.ZERO_EINVAL
     assert zs.lib().zero_span_groups(sp.ctypes.data, sp.size, 3, 64, None, 0, cnt.ctypes.data) == zs.ZERO_EINVAL
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None, reason="hipcc not found")
+def test_piece_orders_are_bijections(tmp_path):
+    """The block-to-piece remappings of launch.h, compiled for the host: bijections
+    of the grid for any size, one contiguous run per XCD, runs of K consecutive
+    pieces, and the identity for K = 1."""
+    exe = str(tmp_path / "piece_orders")
+    csrc = os.path.join(ROOT, "zero_sharded_optimizer_owned_amd", "csrc")
+    res = subprocess.run(["hipcc", "--cuda-host-only", "-x", "hip", "-std=c++17", "-I", csrc,
+                          os.path.join(ROOT, "tests", "host", "piece_orders.cpp"), "-o", exe],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-3000:]
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0 and "clean" in run.stdout, run.stdout[-2000:]

@@ -38,7 +38,7 @@ uint32_t chunk_grid(uint64_t n_pieces, uint32_t requested);
 // stream one source 6% faster and a 1:1 copy 2.4% faster, but lose 1-2% from
 // about ten streams on; kernels opt in where their own A/B says so.
 constexpr uint64_t kXcds = 8;
-__device__ __forceinline__ uint64_t xcd_contiguous(uint64_t b, uint64_t G) {
+__host__ __device__ __forceinline__ uint64_t xcd_contiguous(uint64_t b, uint64_t G) {
   const uint64_t x = b % kXcds, k = b / kXcds, q = G / kXcds, r = G % kXcds;
   return x * q + (x < r ? x : r) + k;
 }
@@ -46,7 +46,7 @@ __device__ __forceinline__ uint64_t xcd_contiguous(uint64_t b, uint64_t G) {
 // Between the two: the XCDs take runs of K consecutive pieces in turn (XCD x
 // gets pieces xK .. xK+K-1, then 8K + xK .. , and so on); a last partial
 // round keeps the plain order.  A bijection of [0, G); K = 1 is the identity.
-__device__ __forceinline__ uint64_t xcd_runs(uint64_t b, uint64_t G, uint64_t K) {
+__host__ __device__ __forceinline__ uint64_t xcd_runs(uint64_t b, uint64_t G, uint64_t K) {
   const uint64_t span = kXcds * K, full = G / span * span;
   if (b >= full) return b;
   return b / span * span + (b % kXcds) * K + (b / kXcds) % K;
