@@ -253,6 +253,23 @@ def test_stage3_storage_matches_oracle_and_printed_example():
             zs.zero3_storage(*bad)
 
 
+def test_stage3_counts_beyond_64_bits_are_erange():
+    """Two tensors of 2^63 elements: every stage-3 total (dense, shard buffer,
+    gathered buffer) is 2^64 at R = 1, one past the largest offset."""
+    big = [1 << 63, 1 << 63]
+    calls = (lambda: zs.zero3_storage(big, 1, [0, 1]),
+             lambda: zs.zero3_gather_spans(big, 1, [1]),
+             lambda: zs.zero3_partition_spans(big, 1, 0))
+    for call in calls:
+        with pytest.raises(zs.ZeroShardError) as ei:
+            call()
+        assert ei.value.code == zs.ZERO_ERANGE
+    # totals just below 2^64 fit, with offsets beyond 2^63
+    fit = [(1 << 63) - 1, 8]
+    spans = zs.zero3_gather_spans(fit, 1, [1])
+    assert [(int(sp["src"]), int(sp["dst"]), int(sp["len"])) for sp in spans] == [((1 << 63) - 1, 0, 8)]
+
+
 def _apply_spans(spans, srcs, dst):
     for sp in spans:
         s, d, n, b = int(sp["src"]), int(sp["dst"]), int(sp["len"]), int(sp["buf"])

@@ -4,6 +4,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "internal.h"
 
@@ -301,6 +302,25 @@ int check_stage3(const uint64_t* numel, uint32_t n_tensors, uint32_t ranks, cons
 
 uint64_t shard_of(uint64_t n, uint32_t ranks) { return n / ranks + (n % ranks != 0); }
 
+// Totals of a stage-3 layout in 128 bits: elements of all tensors, of one
+// rank's shard buffer, and of the live tensors' gathered buffers.  ERANGE when
+// any of them (and so any offset inside them) exceeds 64 bits.
+int stage3_totals(const uint64_t* numel, uint32_t n_tensors, uint32_t ranks, const uint32_t* live,
+                  uint32_t n_live, const char* who, u128* dense, u128* resident, u128* gathered) {
+  u128 d = 0, res = 0, gat = 0;
+  for (uint32_t k = 0; k < n_tensors; ++k) {
+    d += numel[k];
+    res += shard_of(numel[k], ranks);
+  }
+  for (uint32_t i = 0; i < n_live; ++i) gat += (u128)shard_of(numel[live[i]], ranks) * ranks;
+  if (d > (u128)UINT64_MAX || res > (u128)UINT64_MAX || gat > (u128)UINT64_MAX)
+    return fail(ZERO_ERANGE, "%s: counts exceed 64 bits", who);
+  if (dense) *dense = d;
+  if (resident) *resident = res;
+  if (gathered) *gathered = gat;
+  return ZERO_OK;
+}
+
 // Append [src, src+len) -> [dst, dst+len) of buffer `buf`, cut into pieces of at most C.
 void add_spans(uint64_t src, uint64_t dst, uint64_t len, uint32_t buf, uint64_t C, zero_copy_span* out,
                uint64_t capacity, uint64_t* count) {
@@ -339,10 +359,7 @@ extern "C" int zero3_storage(const uint64_t* numel, uint32_t n_tensors, uint32_t
   if (rc) return rc;
   if (!resident || !gathered) return fail(ZERO_EINVAL, "%s: NULL output", who);
   u128 res = 0, gat = 0;
-  for (uint32_t k = 0; k < n_tensors; ++k) res += shard_of(numel[k], ranks);
-  for (uint32_t i = 0; i < n_live; ++i) gat += (u128)shard_of(numel[live[i]], ranks) * ranks;
-  if (res > (u128)UINT64_MAX || gat > (u128)UINT64_MAX)
-    return fail(ZERO_ERANGE, "%s: counts exceed 64 bits", who);
+  if ((rc = stage3_totals(numel, n_tensors, ranks, live, n_live, who, nullptr, &res, &gat))) return rc;
   if (shard_numel)
     for (uint32_t k = 0; k < n_tensors; ++k) shard_numel[k] = shard_of(numel[k], ranks);
   *resident = (uint64_t)res;
@@ -360,13 +377,20 @@ extern "C" int zero3_gather_spans(const uint64_t* numel, uint32_t n_tensors, uin
   if (!n_spans) return fail(ZERO_EINVAL, "%s: n_spans is NULL", who);
   if (max_span == 0) return fail(ZERO_EINVAL, "%s: max_span must be >= 1", who);
   if (capacity > 0 && !out) return fail(ZERO_EINVAL, "%s: out is NULL", who);
+  // every offset below is bounded by the shard-buffer or gathered total
+  if ((rc = stage3_totals(numel, n_tensors, ranks, live, n_live, who, nullptr, nullptr, nullptr)))
+    return rc;
+  std::vector<uint64_t> so(n_tensors);  // shard offset of each tensor
+  for (uint64_t k = 0, acc = 0; k < n_tensors; ++k) {
+    so[k] = acc;
+    acc += shard_of(numel[k], ranks);
+  }
   uint64_t count = 0, gbase = 0;
   for (uint32_t i = 0; i < n_live; ++i) {
     const uint32_t k = live[i];
-    uint64_t so = 0;
-    for (uint32_t j = 0; j < k; ++j) so += shard_of(numel[j], ranks);
     const uint64_t s = shard_of(numel[k], ranks);
-    for (uint32_t r = 0; r < ranks; ++r) add_spans(so, gbase + (uint64_t)r * s, s, r, max_span, out, capacity, &count);
+    for (uint32_t r = 0; r < ranks; ++r)
+      add_spans(so[k], gbase + (uint64_t)r * s, s, r, max_span, out, capacity, &count);
     gbase += (uint64_t)ranks * s;
   }
   return finish_spans(out, capacity, count, n_spans, who);
@@ -383,6 +407,7 @@ extern "C" int zero3_partition_spans(const uint64_t* numel, uint32_t n_tensors, 
   if (rank >= ranks) return fail(ZERO_EINVAL, "%s: rank %u >= ranks %u", who, rank, ranks);
   if (max_span == 0) return fail(ZERO_EINVAL, "%s: max_span must be >= 1", who);
   if (capacity > 0 && !out) return fail(ZERO_EINVAL, "%s: out is NULL", who);
+  if ((rc = stage3_totals(numel, n_tensors, ranks, nullptr, 0, who, nullptr, nullptr, nullptr))) return rc;
   uint64_t count = 0, so = 0, dense = 0;
   for (uint32_t k = 0; k < n_tensors; ++k) {
     const uint64_t s = shard_of(numel[k], ranks);
