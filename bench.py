@@ -62,12 +62,13 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
-    """Hash of the sources of the step kernels (counter records are tied to it)."""
-    from zero_sharded_optimizer_owned_amd.build import CSRC, STEP_SOURCES
+def kernel_source_hash(copy: bool = False) -> str:
+    """Hash of the sources of the step kernels, or of the copy kernels (export,
+    stage-3 gather); counter records are tied to it."""
+    from zero_sharded_optimizer_owned_amd.build import COPY_SOURCES, CSRC, STEP_SOURCES
 
     h = hashlib.sha256()
-    for name in STEP_SOURCES:
+    for name in COPY_SOURCES if copy else STEP_SOURCES:
         h.update(open(os.path.join(CSRC, name), "rb").read())
     return h.hexdigest()[:16]
 
@@ -76,13 +77,13 @@ def kernel_source_hash() -> str:
 WORKLOAD_TAG = {2: "flat-1.5e9-R4", 3: "llama-6.6e9-R8", 4: "flat-7e10-R64", 5: "10k-tensors-2e9-R16"}
 
 
-def traffic_record(name: str):
+def traffic_record(name: str, copy: bool = False):
     """Counter-derived HBM bytes per launch, if taken on the current kernel source."""
     p = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(copy):
         return None
     return rec.get("bytes_per_launch")
 
@@ -596,7 +597,8 @@ def gather3_bench(args, ceil):
                                "(36 tensors) into full padded buffers", "op": "gather3",
                    "gathered_params": g.gathered, "resident_per_rank": g.resident, "spans": int(g.spans.size)},
         "roofline": {"bound": "hbm", "achieved": round(nbytes / (ms / 1e3) / 1e9, 1), "peak": PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(nbytes / (ms / 1e3) / 1e9 / PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(nbytes / (ms / 1e3) / 1e9 / PEAK_GBPS, 4),
+                     "traffic": traffic_record("span_copy_bf16__llama-layers0-3-R8", copy=True),
                      "kernel": "span_kernel<uint16_t>", "kernel_ms": round(ms, 4), "bytes_per_launch": nbytes},
     }
     if ceil:
@@ -721,7 +723,8 @@ def export_bench(w: Workload, args, ceil):
         "config": {"workload": w.name + "; export of the owner's master to dense per-tensor fp32",
                    "config": args.config, "op": "export", "owned_params": n},
         "roofline": {"bound": "hbm", "achieved": round(nbytes / (ms / 1e3) / 1e9, 1), "peak": PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(nbytes / (ms / 1e3) / 1e9 / PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(nbytes / (ms / 1e3) / 1e9 / PEAK_GBPS, 4),
+                     "traffic": traffic_record(f"owner_to_dense__{WORKLOAD_TAG[args.config]}", copy=True),
                      "kernel": "owner_to_dense", "kernel_ms": round(ms, 4), "bytes_per_launch": nbytes},
     }
     if ceil:

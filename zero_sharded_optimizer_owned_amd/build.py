@@ -11,6 +11,8 @@ SOURCES = ("host.cpp", "launch.hip", "step.hip", "copy.hip", "probe.hip")
 # The sources whose kernels make up the optimizer step (hashed to tie counter
 # records to the code they were taken on).
 STEP_SOURCES = ("step.hip", "launch.hip", "launch.h", "internal.h", "scan.h")
+# The same for the copy kernels (checkpoint export/import, stage-3 gather).
+COPY_SOURCES = ("copy.hip", "launch.hip", "launch.h", "internal.h", "scan.h")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 HIPCC_FLAGS = [
