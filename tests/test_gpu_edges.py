@@ -12,6 +12,8 @@
   oracle, with an IEEE (non-power-of-two) divisor too, and a fused check
   whose squared norm matches the oracle's.  This holds only if the kernels
   keep subnormals (no flush to zero) and divide with IEEE rounding.
+* The fused step at extreme step counts and betas, against the oracle to its
+  tolerance: bias corrections tiny, near one or exactly one, and zero betas.
 """
 import math
 
@@ -165,3 +167,47 @@ def test_reduce_of_subnormals_is_bitexact(code, divisor):
     flag, sumsq = oracle.grad_check(want)
     assert int(ov.item()) == flag == 0
     assert math.isclose(ss.item(), sumsq, rel_tol=1e-9, abs_tol=0.0)
+
+
+# (step, beta1, beta2): bias corrections near 0 (betas near 1 early on), near 1
+# (late steps), exactly 1 (beta^t underflows), and betas of 0 (no averaging).
+HYPER_EDGES = [(1, 0.9, 0.999), (3, 0.999, 0.999999), (1_000_000, 0.9, 0.99999), (2 ** 40, 0.8, 0.999),
+               (7, 0.0, 0.0), (2, 0.0, 0.999)]
+
+
+@pytest.mark.parametrize("step,beta1,beta2", HYPER_EDGES)
+def test_fused_step_at_extreme_steps_and_betas(step, beta1, beta2):
+    """The fused step against the oracle (common pre-state, tolerance 1e-6 rel /
+    1e-7 abs, 16-bit copy within 1 ulp), where the host's fp64 bias corrections
+    are tiny, exactly one, or the betas are zero."""
+    import synth
+    from helpers import assert_p16_within_ulp, assert_state_close, gen
+
+    print(f"hyper edges step={step} beta1={beta1} beta2={beta2}", flush=True)
+    numels, R, A, owner = [1000, 37, 5003, 1, 777], 3, 64, 1
+    off, total, b, e = zs.zero_shard_layout(numels, R, A)
+    begin, end = int(b[owner]), int(e[owner])
+    lb = begin & ~7
+    size = end - lb
+    grads = [gen(9, synth.STREAM_GRAD, total, synth.DIST_NORMAL, 1e-3, F16, rank=r) for r in range(R)]
+    w = gen(9, synth.STREAM_MASTER, size, synth.DIST_NORMAL, 0.02, F32)
+    m = gen(9, synth.STREAM_EXP_AVG, size, synth.DIST_NORMAL, 5e-4, F32)
+    v = gen(9, synth.STREAM_EXP_AVG_SQ, size, synth.DIST_SQUARE, 1e-4, F32)
+    hp = dict(lr=1e-3, beta1=beta1, beta2=beta2, eps=1e-8, weight_decay=3e-7, adamw=True)
+    chunks = zs.zero_chunk_table(numels, off, begin, end, 256)
+    dw, dm, dv = to_dev(w, F32), to_dev(m, F32), to_dev(v, F32)
+    p_host = np.zeros(total, dtype=np.uint16)
+    dp = to_dev(p_host, F16)
+    zs.zero_adam_step(chunks_dev=zs.chunks_to_device(chunks), n_chunks=chunks.size, begin=begin, end=end,
+                      master=dw, exp_avg=dm, exp_avg_sq=dv, local_base=lb, step=step,
+                      rank_grads=[to_dev(g, F16) for g in grads], divisor=float(R), param16=dp, **hp)
+    ranges = oracle.real_ranges(numels, list(off), begin, end)
+    oracle.owner_step(ranges, oracle.hyper(step=step, **hp), w, m, v, lb, grads=grads, gdtype=F16,
+                      divisor=float(R), p16=p_host, pdtype=F16)
+    assert_state_close(from_dev(dw), w, "w")
+    assert_state_close(from_dev(dm), m, "m")
+    assert_state_close(from_dev(dv), v, "v")
+    real = np.zeros(total, dtype=bool)
+    for s, t in ranges:
+        real[s:t] = True
+    assert_p16_within_ulp(from_dev(dp)[real], p_host[real], "p16")
