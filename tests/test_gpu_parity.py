@@ -55,7 +55,7 @@ def _rank_inputs(code, R, total, seed=1, scale=1e-3):
 
 
 @pytest.mark.parametrize("code", [F16, BF16, F32])
-@pytest.mark.parametrize("R", [1, 3, 4, 8, 13, 64])
+@pytest.mark.parametrize("R", [1, 3, 4, 8, 13, 16, 24, 64])
 def test_reduce_bitexact(code, R):
     total = 70_001
     begin, n = 13, 50_005          # ragged on both ends
