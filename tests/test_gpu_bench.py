@@ -1,0 +1,59 @@
+"""The benchmark's output contract, checked on a short run of the default workload.
+
+bench.py runs in a child process (as the benchmark is run), for two timed steps
+of the default configuration with a one-second CPU-oracle sample, and its one
+JSON line must carry every field the contract names, consistent with itself:
+value = owned parameters / step time, roofline.frac = achieved / peak, the
+dominant kernel's algorithmic bytes = its elements x bytes per element, and a
+CPU baseline of the oracle.
+"""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def test_default_bench_line_keeps_the_contract():
+    print("bench.py --steps 2 --warmup 1 --no-ceiling --cpu-seconds 1", flush=True)
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "2", "--warmup", "1",
+                          "--no-ceiling", "--cpu-seconds", "1"], capture_output=True, text=True, timeout=110,
+                         cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-2000:]
+    lines = [ln for ln in res.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1, "bench.py prints exactly one line"
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 2 and d["warmup"] == 1
+    assert d["higher_is_better"] is True and d["scaling"] == "weak" and d["vs_baseline"] is None
+    assert d["unit"] == "params/s" and d["dtype"] == "f32" and d["data"] == "synthetic"
+    cfg = d["config"]
+    assert "workload" in cfg and cfg["owned_params"] == 375_000_000
+    # value: owned parameters updated per second of the mean step
+    assert d["value"] == pytest.approx(cfg["owned_params"] / (d["ms_per_step"] * 1e-3), rel=1e-3)
+    r = d["roofline"]
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert r["bytes_per_launch"] == r["elements_per_launch"] * r["bytes_per_element"] == 375_000_000 * 34
+    assert r["achieved"] == pytest.approx(r["bytes_per_launch"] / (r["kernel_ms"] * 1e-3) / 1e9, rel=1e-3)
+    assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], abs=1e-4)
+    assert 0.3 < r["frac"] < 1.0
+    # the counter record matches the current kernel source, so traffic is reported
+    assert r["traffic"] is not None and r["traffic"] >= r["bytes_per_launch"]
+    c = d["cpu_baseline"]
+    assert c["kind"] == "oracle" and c["unit"] == "params/s" and c["value"] > 0 and c["cores"] >= 1
+    assert c["sample"]
