@@ -111,7 +111,9 @@ typedef struct {
  * small tensors still make full-size chunks -- are cut at the flat multiples
  * of `max_chunk_elems`, so interior cuts fall on 128-bit vector boundaries.
  * Chunks come out in increasing flat order and cover every real element of
- * the range exactly once.
+ * the range exactly once.  Padding follows the reading stated at
+ * zero_shard_layout (the pages leave it open): every tensor, the last one
+ * included, is padded to the alignment, and the padding belongs to no chunk.
  *
  * numel, tensor_offset [n_tensors] in: as from zero_shard_layout (offsets
  *                      increasing, tensors not overlapping)
@@ -125,6 +127,25 @@ typedef struct {
 int zero_chunk_table(const uint64_t *numel, const uint64_t *tensor_offset, uint32_t n_tensors,
                      uint64_t begin, uint64_t end, uint32_t max_chunk_elems, zero_chunk *out,
                      uint64_t capacity, uint64_t *n_chunks);
+
+/* ----------------------------------------------------------------------------
+ * zero_dense_offsets -- where each tensor starts in the dense layout.
+ *
+ * [Deep dive] "Resume training and export weights separately": exporting
+ * consolidates the fp32 weights into per-tensor form, without the flat
+ * buffer's padding.  dense_offset[k] = numel[0] + ... + numel[k-1]; the
+ * dense buffer holds dense_total = numel[0] + ... + numel[n_tensors-1]
+ * elements.  These are the offsets zero_owner_to_dense / zero_dense_to_owner
+ * take (as a device table) to address the dense buffer.
+ *
+ * numel[n_tensors]         in : element counts, all > 0
+ * dense_offset[n_tensors]  out: caller-owned host array
+ * dense_total              out
+ * Errors: EINVAL for a zero count or NULL pointers; ERANGE if the total
+ * exceeds 64 bits (nothing is written then).
+ * -------------------------------------------------------------------------- */
+int zero_dense_offsets(const uint64_t *numel, uint32_t n_tensors, uint64_t *dense_offset,
+                       uint64_t *dense_total);
 
 /* Exact byte count num/den, reduced to lowest terms. */
 typedef struct {
@@ -151,9 +172,9 @@ int zero_state_bytes(uint64_t params, uint64_t ranks, uint32_t param_bytes, uint
 /* ----------------------------------------------------------------------------
  * zero_reduce_owned -- the owner's reduced gradient, in fp32.
  *
- * [Deep dive] "Reduce first, then update the owned slice" (the reference
- * reduce-scatter: reduce across ranks, keep the owned indices; equally
- * weighted mean).  For every flat index f in [begin, begin + n), with
+ * [Deep dive] "Reduce first, then update the owned slice": the owner's
+ * share of a reduce-scatter, i.e. the equally weighted mean over ranks,
+ * formed only at the indices it owns.  For every flat index f in [begin, begin + n), with
  * o = out[f - out_base]:
  *   s = (accumulate == 1 ? o : +0.0f);
  *   for r = 0 .. R-1:  s = s + (float) rank_grads[r][f - grad_base];   (fp32)

@@ -65,10 +65,6 @@ def adam_step(weight: float, first: float, second: float, gradient: float, step:
     return weight - lr * mhat / (math.sqrt(vhat) + eps), first, second
 
 
-def _positive_ints(*xs) -> bool:
-    return all(type(x) is int and x > 0 for x in xs)
-
-
 def owner_ranges(parameters: int, ranks: int) -> List[range]:
     """Contiguous ownership: owner r holds ``[floor(P*r/R), floor(P*(r+1)/R))``.
 
@@ -84,67 +80,93 @@ def pages_gradient(i: int, r: int, step: int) -> float:
 
 
 def compare_owned_updates(parameters: int, ranks: int, steps: int, grad=pages_gradient):
-    """Unsharded Adam on the rank-mean gradient vs owner-sharded Adam.
+    """Adam on the rank-mean gradient, run once unsharded and once owner by owner.
 
-    [Deep dive] "Reduce first, then update the owned slice": weights start at
-    ``0.1*i`` with zero moments; every step each rank contributes a gradient,
-    the unsharded run applies Adam to the mean over ranks; each owner reduces
-    only its own indices and applies Adam once to them.  Returns
-    ``(reference, reconstructed)``, lists of ``(w, m, v)`` per parameter.
+    [Deep dive] "Reduce first, then update the owned slice": weight i starts at
+    ``0.1*i`` with both moments zero; at every step each rank supplies a
+    gradient for every parameter.  The unsharded run updates every parameter
+    from the mean over ranks.  In the sharded run each owner keeps the state of
+    its contiguous index range only, forms the same mean for those indices
+    (its share of a reduce-scatter) and updates them once.  Returns
+    ``(unsharded, sharded)``: the ``(w, m, v)`` of every parameter, the sharded
+    list read owner after owner.
     """
-    if not _positive_ints(parameters, ranks, steps):
-        raise ValueError("parameters, ranks, and steps must be positive integers")
-    reference = [(0.1 * i, 0.0, 0.0) for i in range(parameters)]
-    owners = owner_ranges(parameters, ranks)
-    sharded = [{i: reference[i] for i in own} for own in owners]
+    for label, x in (("parameters", parameters), ("ranks", ranks), ("steps", steps)):
+        if type(x) is not int or x <= 0:
+            raise ValueError(f"{label}: expected an int above zero, got {x!r}")
+
+    def initial(i):
+        return 0.1 * i, 0.0, 0.0
+
+    def rank_mean(g, i):
+        total = 0.0
+        for r in range(ranks):
+            total += g[r][i]
+        return total / ranks
+
+    unsharded = [initial(i) for i in range(parameters)]
+    # owner r: (its index range, the states of those indices in range order)
+    owned = [(span, [initial(i) for i in span]) for span in owner_ranges(parameters, ranks)]
     for t in range(1, steps + 1):
-        local = [[grad(i, r, t) for i in range(parameters)] for r in range(ranks)]
-        mean = [sum(local[r][i] for r in range(ranks)) / ranks for i in range(parameters)]
-        reference = [adam_step(*reference[i], mean[i], t) for i in range(parameters)]
-        for r, own in enumerate(sharded):
-            reduced = {i: sum(row[i] for row in local) / ranks for i in own}
-            sharded[r] = {i: adam_step(*own[i], reduced[i], t) for i in own}
-    reconstructed = [state for own in sharded for state in own.values()]
-    return reference, reconstructed
+        g = [[grad(i, r, t) for i in range(parameters)] for r in range(ranks)]  # g[r][i]
+        for i in range(parameters):
+            unsharded[i] = adam_step(*unsharded[i], rank_mean(g, i), t)
+        for span, states in owned:
+            for k, i in enumerate(span):
+                states[k] = adam_step(*states[k], rank_mean(g, i), t)
+    sharded = [state for _, states in owned for state in states]
+    return unsharded, sharded
 
 
 def state_bytes(parameters: int, ranks: int, param: int = 2, grad: int = 2,
                 optimizer: int = 12) -> Dict[str, Fraction]:
     """Idealised per-rank persistent bytes for DP and ZeRO-1/2/3, as exact fractions.
 
-    [Deep dive] "Count state before choosing a stage" (and [ZeRO Q&A]
-    "Memory Footprint Reduction Matrix"): DP replicates everything; ZeRO-1
-    shards the optimizer state; ZeRO-2 also the gradients; ZeRO-3 also the
-    parameters.  Inputs must be positive integers.
+    [Deep dive] "Count state before choosing a stage" and [ZeRO Q&A] "Memory
+    Footprint Reduction Matrix": a parameter carries three parts -- the 16-bit
+    compute copy (``param`` bytes), its gradient (``grad``) and the optimizer
+    state with the fp32 master (``optimizer``).  Stage k divides a part among
+    the ranks once k reaches the stage that first shards it (optimizer state
+    from stage 1, gradients from stage 2, parameters at stage 3); DP (stage 0)
+    replicates all three.  Every input must be an int above zero.
     """
-    if not _positive_ints(parameters, ranks, param, grad, optimizer):
-        raise ValueError("counts and byte widths must be positive integers")
-    shard = Fraction(parameters, ranks)
-    return {
-        "DP": Fraction(parameters * (param + grad + optimizer)),
-        "ZeRO-1": parameters * (param + grad) + shard * optimizer,
-        "ZeRO-2": parameters * param + shard * (grad + optimizer),
-        "ZeRO-3": shard * (param + grad + optimizer),
-    }
+    widths = {"param": param, "grad": grad, "optimizer": optimizer}
+    for label, x in (("parameters", parameters), ("ranks", ranks), *widths.items()):
+        if type(x) is not int or x <= 0:
+            raise ValueError(f"{label}: expected an int above zero, got {x!r}")
+    first_sharded = {"optimizer": 1, "grad": 2, "param": 3}
+    out = {}
+    for stage, name in enumerate(("DP", "ZeRO-1", "ZeRO-2", "ZeRO-3")):
+        total = Fraction(0)
+        for part, width in widths.items():
+            copies = Fraction(1, ranks) if stage >= first_sharded[part] else Fraction(1)
+            total += parameters * width * copies
+        out[name] = total
+    return out
 
 
 def parameter_storage(layer_sizes: Sequence[int], ranks: int, live_layers: Sequence[int]):
     """ZeRO-3 parameter elements: resident shards + separate full gather buffers.
 
-    [Deep dive] "Stage 3 needs a live working set": each tensor's shard is
-    ``ceil(n/R)`` elements; a live (gathered) tensor adds a separate padded
-    buffer of ``R * ceil(n/R)`` elements.  Returns ``(resident, gathered, total)``.
+    [Deep dive] "Stage 3 needs a live working set": each tensor's shard holds
+    ``ceil(n/R)`` whole elements; a live (gathered) tensor also needs its own
+    padded buffer of ``R * ceil(n/R)`` elements, which does not alias the
+    shard.  Returns ``(resident, gathered, total)`` element counts.
     """
-    if type(ranks) is not int or ranks <= 0:
-        raise ValueError("ranks must be a positive integer")
-    if not layer_sizes or any(type(n) is not int or n <= 0 for n in layer_sizes):
-        raise ValueError("tensor sizes must be positive integers")
-    if any(type(i) is not int or not 0 <= i < len(layer_sizes) for i in live_layers) or \
-            len(set(live_layers)) != len(live_layers):
-        raise ValueError("live tensor indices must be distinct and in range")
-    shards = [-(-n // ranks) for n in layer_sizes]
-    resident = sum(shards)
-    gathered = sum(shards[i] * ranks for i in live_layers)
+    if type(ranks) is not int or ranks < 1:
+        raise ValueError(f"ranks: expected an int of at least 1, got {ranks!r}")
+    sizes = list(layer_sizes)
+    if not sizes or not all(type(n) is int and n >= 1 for n in sizes):
+        raise ValueError("layer_sizes: every tensor needs an int element count of at least 1")
+    live = list(live_layers)
+    if len(set(live)) != len(live) or not all(type(k) is int and 0 <= k < len(sizes) for k in live):
+        raise ValueError("live_layers: expected distinct indices into layer_sizes")
+    resident = gathered = 0
+    for k, n in enumerate(sizes):
+        shard = n // ranks + (1 if n % ranks else 0)  # rounded up to whole elements
+        resident += shard
+        if k in live:
+            gathered += ranks * shard
     return resident, gathered, resident + gathered
 
 
@@ -219,7 +241,10 @@ def real_ranges(numels: Sequence[int], offsets: Sequence[int], begin: int, end: 
 
 
 def dense_offsets(numels: Sequence[int]) -> List[int]:
-    """Start of each tensor in the dense (unpadded) concatenation of all tensors."""
+    """Start of each tensor in the dense (unpadded) concatenation of all tensors:
+    the layout an exported fp32 checkpoint uses ([Deep dive] "Resume training
+    and export weights separately": export consolidates the weights, padding
+    dropped)."""
     out, pos = [], 0
     for n in numels:
         out.append(pos)

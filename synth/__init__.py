@@ -156,9 +156,59 @@ LIB_PATH = _os.path.join(_HERE, "libzero_synth.so")
 _lib = None
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the device generator for gfx950 into synth/libzero_synth.so."""
+HOST_LIB_PATH = _os.path.join(_HERE, "libsynth_host.so")
+_host_lib = None
+
+
+def build_host() -> str:
+    """Compile the multi-threaded host generator (gcc, OpenMP) into synth/libsynth_host.so."""
     import subprocess
+
+    src = _os.path.join(_HERE, "csrc", "synth_host.c")
+    tmp = HOST_LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared",
+           "-Wall", src, "-o", tmp, "-lm"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("building the host generator failed:\n" + res.stderr)
+    _os.replace(tmp, HOST_LIB_PATH)
+    return HOST_LIB_PATH
+
+
+def _load_host():
+    global _host_lib
+    if _host_lib is None:
+        if not _os.path.exists(HOST_LIB_PATH):
+            build_host()
+        lib = _ct.CDLL(HOST_LIB_PATH)
+        lib.synth_host_fill.restype = _ct.c_int
+        lib.synth_host_fill.argtypes = [_ct.c_void_p, _ct.c_int, _ct.c_uint64, _ct.c_uint64, _ct.c_uint64,
+                                        _ct.c_int, _ct.c_float]
+        _host_lib = lib
+    return _host_lib
+
+
+def host_values(key: int, start: int, count: int, dist: int, scale: float, dtype: int,
+                out: np.ndarray = None) -> np.ndarray:
+    """Elements [start, start + count) of a stream in storage form, on all host
+    cores: the same bits as ``values(key, arange(start, start + count), ...)``."""
+    want = np.float32 if dtype == F32 else np.uint16
+    if out is None:
+        out = np.empty(count, dtype=want)
+    if out.dtype != want or out.size != count or not out.flags["C_CONTIGUOUS"]:
+        raise ValueError("out must be a contiguous array of the storage dtype and length count")
+    c = float(_SCALE[dist](scale))
+    rc = _load_host().synth_host_fill(_ct.c_void_p(out.ctypes.data), dtype, count, key, start, dist, c)
+    if rc != 0:
+        raise ValueError(f"synth_host_fill rejected its arguments ({rc})")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the device generator for gfx950 into synth/libzero_synth.so (and the host twin)."""
+    import subprocess
+
+    build_host()
 
     src = _os.path.join(_HERE, "csrc", "synth_device.hip")
     tmp = LIB_PATH + ".tmp"

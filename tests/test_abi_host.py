@@ -47,6 +47,19 @@ def test_layout_matches_oracle():
         assert list(zip(b.tolist(), e.tolist())) == owners
 
 
+def test_dense_offsets_match_oracle():
+    rnd = random.Random(5)
+    for _ in range(300):
+        numels = [rnd.randrange(1, 1 << 40) for _ in range(rnd.randrange(1, 40))]
+        off, total = zs.zero_dense_offsets(numels)
+        assert [int(x) for x in off] == oracle.dense_offsets(numels)
+        assert total == sum(numels)
+    with pytest.raises(zs.ZeroShardError):
+        zs.zero_dense_offsets([4, 0, 3])
+    with pytest.raises(zs.ZeroShardError):
+        zs.zero_dense_offsets([2 ** 63, 2 ** 63])
+
+
 def test_layout_large_counts_use_wide_products():
     # 7e10 elements over 64 owners: P * r exceeds 2^64 only for huge P; check the
     # formula against Python integers near the top of the range too.

@@ -85,3 +85,18 @@ def test_layout_with_one_tensor_and_align_one_is_the_page_formula():
 def test_layout_rejects(args):
     with pytest.raises(ValueError):
         oracle.layout(*args)
+
+
+def test_dense_offsets_against_a_labelled_concatenation():
+    """The dense layout is the tensors laid end to end: build that buffer element by
+    element with each element labelled (tensor, index) and find where every
+    tensor's first element landed."""
+    rnd = random.Random(17)
+    for _ in range(300):
+        numels = [rnd.randrange(1, 50) for _ in range(rnd.randrange(1, 9))]
+        dense = [(k, j) for k, n in enumerate(numels) for j in range(n)]
+        want = [dense.index((k, 0)) for k in range(len(numels))]
+        assert oracle.dense_offsets(numels) == want
+        # and every element sits at its tensor's start plus its index
+        off = oracle.dense_offsets(numels)
+        assert all(dense[off[k] + j] == (k, j) for k, n in enumerate(numels) for j in range(n))

@@ -98,14 +98,20 @@ PY_MUTANTS = {
     "ceil ownership": ("owner_ranges", "parameters * r // ranks", "(parameters * r + ranks - 1) // ranks"),
     "last tensor unpadded": ("layout", "total += -(-n // align) * align", "total += n if n == numels[-1] else -(-n // align) * align"),
     "no padding": ("layout", "total += -(-n // align) * align", "total += n"),
-    "ZeRO-2 keeps full grads": ("state_bytes", '"ZeRO-2": parameters * param + shard * (grad + optimizer)',
-                                '"ZeRO-2": parameters * (param + grad) + shard * optimizer'),
-    "ZeRO-1 shards params": ("state_bytes", '"ZeRO-1": parameters * (param + grad) + shard * optimizer',
-                             '"ZeRO-1": parameters * grad + shard * (param + optimizer)'),
+    "ZeRO-2 keeps full grads": ("state_bytes", '"grad": 2', '"grad": 3'),
+    "ZeRO-1 shards params": ("state_bytes", '"param": 3', '"param": 1'),
+    "DP shards the optimizer state": ("state_bytes", '"optimizer": 1', '"optimizer": 0'),
     "bias correction with beta1": ("adam_step", "vhat = second / (1.0 - beta2 ** step)",
                                    "vhat = second / (1.0 - beta1 ** step)"),
-    "floor shards in stage 3": ("parameter_storage", "shards = [-(-n // ranks) for n in layer_sizes]",
-                                "shards = [n // ranks for n in layer_sizes]"),
+    "floor shards in stage 3": ("parameter_storage", "shard = n // ranks + (1 if n % ranks else 0)",
+                                "shard = n // ranks"),
+    "gather buffer aliases the shard": ("parameter_storage", "gathered += ranks * shard",
+                                        "gathered += (ranks - 1) * shard"),
+    "owner updates from one rank's gradient": ("compare_owned_updates",
+                                               "states[k] = adam_step(*states[k], rank_mean(g, i), t)",
+                                               "states[k] = adam_step(*states[k], g[0][i], t)"),
+    "rank mean over one rank too many": ("compare_owned_updates", "return total / ranks",
+                                         "return total / (ranks + 1)"),
     "clip never clamps": ("clip_coef", "return min(1.0, max_norm / (math.sqrt(sumsq) + eps))",
                           "return max_norm / (math.sqrt(sumsq) + eps)"),
     "stage-3 shard starts at the floor split": ("stage3_shards", "e = r * s + j", "e = r * n // ranks + j"),

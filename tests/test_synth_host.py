@@ -53,3 +53,21 @@ def test_log_uniform_sizes():
     assert s.min() >= 64 and s.max() <= 1 << 24
     logs = np.log(s.astype(np.float64))
     assert abs(logs.mean() - (math.log(64) + math.log(1 << 24)) / 2) < 0.1
+
+
+def test_threaded_host_generator_matches_numpy():
+    """The C host generator (all host cores) gives the numpy generator's bits for
+    every dtype and recipe, including fp16 overflow to infinity (scale 3e4) and
+    fp16 / bf16 subnormals (scale 1e-6, 1e-40)."""
+    cases = [(synth.DIST_NORMAL, 1e-3), (synth.DIST_NORMAL, 65.536), (synth.DIST_UNIFORM, 0.3),
+             (synth.DIST_SQUARE, 1e-4), (synth.DIST_NORMAL, 3e4), (synth.DIST_UNIFORM, 7e4),
+             (synth.DIST_NORMAL, 1e-6), (synth.DIST_NORMAL, 1e-40)]
+    with np.errstate(over="ignore"):
+        for dist, scale in cases:
+            for dt in (synth.F16, synth.BF16, synth.F32):
+                key = synth.stream_key(3, synth.STREAM_GRAD, 5, 2)
+                want = synth.values(key, synth.arange(1000, 101_000), dist, scale, dt)
+                got = synth.host_values(key, 1000, 100_000, dist, scale, dt)
+                if dt == synth.F32:
+                    want, got = want.view(np.uint32), got.view(np.uint32)
+                assert np.array_equal(got, want), (dist, scale, dt)

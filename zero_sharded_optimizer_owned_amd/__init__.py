@@ -27,7 +27,7 @@ ZERO_OK, ZERO_EINVAL, ZERO_ERANGE, ZERO_EHIP = 0, -1, -2, -3
 ZERO_NONE, ZERO_F16, ZERO_BF16, ZERO_F32 = 0, 1, 2, 3
 ZERO_MAX_RANKS = 256
 
-EXPORTED = ("zero_last_error", "zero_shard_layout", "zero_chunk_table", "zero_state_bytes",
+EXPORTED = ("zero_last_error", "zero_shard_layout", "zero_chunk_table", "zero_dense_offsets", "zero_state_bytes",
             "zero_reduce_owned", "zero_grad_check", "zero_clip_coef", "zero_adam_step",
             "zero_owner_to_dense", "zero_dense_to_owner", "zero3_storage", "zero3_gather_spans",
             "zero3_partition_spans", "zero_copy_spans", "zero_stream_probe",
@@ -78,6 +78,7 @@ def load(path: str):
         getattr(L, name).restype = I
     L.zero_shard_layout.argtypes = [P, U32, U32, U32, P, P, P, P]
     L.zero_chunk_table.argtypes = [P, P, U32, U64, U64, U32, P, U64, P]
+    L.zero_dense_offsets.argtypes = [P, U32, P, P]
     L.zero_state_bytes.argtypes = [U64, U64, U32, U32, U32, P]
     L.zero_reduce_owned.argtypes = [P, U32, I, U64, U64, U64, F, I, P, U64, P, P, P, ct.c_size_t, P]
     L.zero_grad_check.argtypes = [P, U64, P, P, P, ct.c_size_t, P]
@@ -144,6 +145,15 @@ def zero_chunk_table(numels: Sequence[int], offsets: Sequence[int], begin: int, 
     _check(lib().zero_chunk_table(_p(n), _p(off), n.size, begin, end, max_chunk,
                                   _p(out) if out.size else None, out.size, _p(count)))
     return out
+
+
+def zero_dense_offsets(numels: Sequence[int]):
+    """(start of each tensor in the dense unpadded layout, dense total)."""
+    n = _u64(numels)
+    off = np.zeros(max(1, n.size), dtype=np.uint64)
+    total = np.zeros(1, dtype=np.uint64)
+    _check(lib().zero_dense_offsets(_p(n), n.size, _p(off), _p(total)))
+    return off[: n.size], int(total[0])
 
 
 def groups_pay(n_groups: int, n_items: int) -> bool:
@@ -525,10 +535,9 @@ class OwnerShard:
             self.groups_dev = torch.from_numpy(self.groups.astype(np.int64)).to(self.device)
         self.n_real = int(self.chunks["len"].sum()) if self.chunks.size else 0
         self.align = align
-        self.dense_total = int(sum(self.numels))
-        dense_off = np.concatenate([[0], np.cumsum(self.numels)[:-1]]).astype(np.int64)
+        self.dense_offsets, self.dense_total = zero_dense_offsets(self.numels)
         self.tensor_offset_dev = torch.from_numpy(self.offsets.astype(np.int64)).to(self.device)
-        self.dense_offset_dev = torch.from_numpy(dense_off).to(self.device)
+        self.dense_offset_dev = torch.from_numpy(self.dense_offsets.astype(np.int64)).to(self.device)
 
     def _group_args(self) -> dict:
         if self.groups_dev is None:

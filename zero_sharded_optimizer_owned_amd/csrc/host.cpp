@@ -68,6 +68,31 @@ extern "C" int zero_shard_layout(const uint64_t* numel, uint32_t n_tensors, uint
   return ZERO_OK;
 }
 
+// Dense (unpadded) start of every tensor: the running sum of the sizes before
+// it ([Deep dive] "Resume training and export weights separately": an export
+// consolidates the weights without the layout's padding).
+extern "C" int zero_dense_offsets(const uint64_t* numel, uint32_t n_tensors, uint64_t* dense_offset,
+                                  uint64_t* dense_total) {
+  zs::clear_error();
+  if (n_tensors > 0 && (!numel || !dense_offset))
+    return fail(ZERO_EINVAL, "zero_dense_offsets: NULL tensor arrays");
+  if (!dense_total) return fail(ZERO_EINVAL, "zero_dense_offsets: dense_total is NULL");
+  u128 total = 0;
+  for (uint32_t k = 0; k < n_tensors; ++k) {
+    if (numel[k] == 0) return fail(ZERO_EINVAL, "zero_dense_offsets: tensor %u has 0 elements", k);
+    total += numel[k];
+    if (total > (u128)UINT64_MAX)
+      return fail(ZERO_ERANGE, "zero_dense_offsets: dense total exceeds 64 bits");
+  }
+  uint64_t pos = 0;
+  for (uint32_t k = 0; k < n_tensors; ++k) {
+    dense_offset[k] = pos;
+    pos += numel[k];
+  }
+  *dense_total = pos;
+  return ZERO_OK;
+}
+
 extern "C" int zero_chunk_table(const uint64_t* numel, const uint64_t* tensor_offset,
                                 uint32_t n_tensors, uint64_t begin, uint64_t end,
                                 uint32_t max_chunk_elems, zero_chunk* out, uint64_t capacity,
