@@ -2,20 +2,23 @@
 
 One step = one pass of the owner's whole hot path over one batch of synthetic
 input (inputs resident in HBM before the timed region):
-  --config 2 (default): 1.5e9-parameter flat buffer, R=4, owner 1 (3.75e8
-      parameters): fused fp16 rank reduce + AdamW + fp16 write-back, one launch.
+  --config 4 (default): 7e10-parameter flat buffer, R=64, owner 1 (1.09375e9
+      parameters), the largest configuration that fits one GPU: fp16 grads
+      scaled by 2^16; reduce + overflow/norm check, host skip/clip decision,
+      AdamW from the stored fp32 gradient; inf/NaN injected in one step of
+      every four (those steps are skipped and count no updated parameters).
+  --config 2: 1.5e9-parameter flat buffer, R=4, owner 1 (3.75e8 parameters):
+      fused fp16 rank reduce + AdamW + fp16 write-back, one launch.
   --config 3: Llama-style 289-tensor list (6,607,339,520 parameters), 64-element
       alignment, R=8, owner 1: fused bf16 reduce + AdamW + bf16 write-back.
-  --config 4: 7e10 flat, R=64, owner 1 (1.09375e9): fp16 grads scaled by 2^16;
-      reduce + overflow/norm check, host skip/clip decision, AdamW from the
-      stored fp32 gradient; inf/NaN injected in one step of every four.
   --config 5: 10,000 log-uniform tensors (~2e9), R=16: eight bf16 microstep
       accumulations into the local fp32 buffer, then the owner's fused
       fp32-rank reduce + AdamW + bf16 write-back.
 
 Prints one JSON line: owned parameters updated per second, achieved HBM GB/s of
 the dominant kernel against the 8 TB/s peak, and the CPU oracle timed on a
-bounded sample of the same workload.
+bounded sample of the same workload (with its GB/s and the GPU's speed-up
+over it).
 """
 from __future__ import annotations
 
@@ -42,7 +45,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4, 5))
+    ap.add_argument("--config", type=int, default=4, choices=(2, 3, 4, 5))
     ap.add_argument("--schedule", default="accumulate", choices=("accumulate", "per-backward"),
                     help="config 5 only: accumulate microsteps locally then reduce (default), or reduce "
                          "every microstep and add the owned mean to an fp32 accumulator")
@@ -90,10 +93,63 @@ def traffic_record(name: str, copy: bool = False):
 
 # ---------------------------------------------------------------- workloads
 # read:write streams of equal size whose byte mix matches each dominant kernel's
-# algorithmic traffic per parameter (e.g. config 2: 20 B read, 14 B written)
-PROBE_MIX = {"adam_step_f16_f16": (10, 7), "adam_step_bf16_bf16": (2, 1), "reduce_check_f16_r64": (33, 1),
+# algorithmic traffic per parameter (e.g. config 2: 20 B read, 14 B written);
+# for the 64-rank reduce also its structure: 64 sources of 2 bytes per
+# parameter, and its 4-byte destination as two streams of 2 bytes
+PROBE_MIX = {"adam_step_f16_f16": (10, 7), "adam_step_bf16_bf16": (2, 1), "reduce_check_f16_r64": (64, 2),
              "accumulate_bf16": (3, 2), "reduce_add_mean_bf16_r16": (9, 1), "owner_to_dense": (1, 1),
              "span_kernel<uint16_t>": (1, 1)}
+
+
+# each dominant kernel's exact stream structure: the widths of its source and
+# destination streams (1: 16-bit data, 16 bytes per 8 elements; 2: fp32 data,
+# 32 bytes per 8 elements), as zero_stream_probe takes them
+PROBE_STRUCTURE = {
+    "adam_step_f16_f16": ([1] * 4 + [2] * 3, [2] * 3 + [1]),      # 4 ranks, w m v in; w m v p16 out
+    "adam_step_bf16_bf16": ([1] * 8 + [2] * 3, [2] * 3 + [1]),    # 8 ranks, w m v in; w m v p16 out
+    "reduce_check_f16_r64": ([1] * 64, [2]),                      # 64 ranks in; fp32 g out
+    "accumulate_bf16": ([1, 2], [2]),                             # bf16 g and fp32 acc in; acc out
+    "reduce_add_mean_bf16_r16": ([1] * 16 + [2], [2]),            # 16 ranks and acc in; acc out
+    "owner_to_dense": ([2], [2]),
+    "span_kernel<uint16_t>": ([1], [1]),
+}
+
+
+def structure_name(kname: str) -> str:
+    src, dst = PROBE_STRUCTURE[kname]
+    part = lambda ws: "+".join(f"{ws.count(w)}x{w}" for w in (1, 2) if ws.count(w))
+    return f"{part(src)}:{part(dst)}"
+
+
+def probe_structure_gbps(kname: str, elements: int, launches: int = 3, reps: int = 3) -> float:
+    """HBM GB/s of the streaming probe with the kernel's exact stream structure
+    (PROBE_STRUCTURE) at the kernel's own size: `elements` 8-element units per
+    stream, i.e. the kernel's algorithmic bytes per launch; best of both piece
+    orders."""
+    import torch
+
+    import zero_sharded_optimizer_owned_amd as zs
+
+    src_w, dst_w = PROBE_STRUCTURE[kname]
+    unit = elements // 8 * 16  # bytes per width unit: 2 bytes per element
+    srcs = [torch.zeros(unit * w, dtype=torch.uint8, device="cuda") for w in src_w]
+    dsts = [torch.empty(unit * w, dtype=torch.uint8, device="cuda") for w in dst_w]
+    best = float("inf")
+    for order in (0, 1):
+        for _ in range(3):
+            zs.zero_stream_probe(srcs, dsts, order, src_widths=src_w, dst_widths=dst_w)
+        for _ in range(reps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            s.record()
+            for _ in range(launches):
+                zs.zero_stream_probe(srcs, dsts, order, src_widths=src_w, dst_widths=dst_w)
+            e.record()
+            torch.cuda.synchronize()
+            best = min(best, s.elapsed_time(e) / launches)
+    del srcs, dsts
+    torch.cuda.empty_cache()
+    return unit * (sum(src_w) + sum(dst_w)) / (best / 1e3) / 1e9
 
 
 def probe_gbps(n_src: int, n_dst: int, total_bytes: float = 8e9, launches: int = 5, reps: int = 3) -> float:
@@ -137,18 +193,44 @@ def step_stats(ms: list) -> dict | None:
             "mean": round(sum(v) / len(v), 4)}
 
 
-def ceilings(kname: str) -> dict:
+def ceilings(kname: str, elements: int) -> dict:
     """Measured ceilings for the dominant kernel: one stream read, one written,
-    a plain copy, and the probe with the kernel's own read:write mix."""
+    a plain copy, the probe with the kernel's own read:write byte mix over
+    equal streams, and the probe with the kernel's exact stream structure and
+    size (``elements`` per stream)."""
     n_src, n_dst = PROBE_MIX[kname]
     return {"read_gbps": round(probe_gbps(1, 0), 1), "write_gbps": round(probe_gbps(0, 1), 1),
             "copy_gbps": round(probe_gbps(1, 1), 1), "mix": f"{n_src}:{n_dst}",
-            "mix_gbps": round(probe_gbps(n_src, n_dst), 1), "kernel": "zero_stream_probe"}
+            "mix_gbps": round(probe_gbps(n_src, n_dst), 1), "structure": structure_name(kname),
+            "structure_gbps": round(probe_structure_gbps(kname, elements), 1), "kernel": "zero_stream_probe"}
 
 
 def with_ceiling(roofline: dict, ceil: dict) -> dict:
     a = roofline["achieved"]
-    return dict(ceil, frac_of_copy=round(a / ceil["copy_gbps"], 4), frac_of_mix=round(a / ceil["mix_gbps"], 4))
+    return dict(ceil, frac_of_copy=round(a / ceil["copy_gbps"], 4), frac_of_mix=round(a / ceil["mix_gbps"], 4),
+                frac_of_structure=round(a / ceil["structure_gbps"], 4))
+
+
+def dominant_elements(args) -> int:
+    """Elements the dominant kernel of a run processes per launch, from the layout
+    alone (the ceilings are measured before the workload takes its memory)."""
+    import zero_sharded_optimizer_owned_amd as zs
+
+    if args.op == "gather3":
+        _, _, gathered = zs.zero3_storage(llama_numels(), 8, list(range(1, 37)))
+        return gathered
+    if args.op == "small":
+        numels, R = [100] * 2_000_000, 4
+    else:
+        numels, R = {2: ([1_500_000_000], 4), 3: (llama_numels(), 8), 4: ([70_000_000_000], 64),
+                     5: (config5_numels(), 16)}[args.config]
+    off, total, b, e = zs.zero_shard_layout(numels, R, 64)
+    if args.config == 5 and args.schedule == "accumulate" and args.op == "step":
+        return total
+    begin, end = int(b[1]), int(e[1])
+    if (args.config == 4 or args.schedule == "per-backward") and args.op == "step":
+        return end - begin
+    return sum(max(0, min(end, int(o) + n) - max(begin, int(o))) for o, n in zip(off, numels))
 
 
 def llama_numels():
@@ -242,6 +324,7 @@ class Workload:
         elif cfg == 5:
             self._setup_microsteps(seed)
         self.t = FIRST_STEP
+        self.max_norm = 1.0  # config 4's clip threshold
         self.calls = 0
         self.skipped = 0
         self.kernel_bytes = self.algorithmic_bytes()
@@ -375,7 +458,7 @@ class Workload:
                 self.grads[17][777_777] = float("nan")
             # reduce + check, 16 bytes to the host, then AdamW from g unless overflowed
             updated, _ = sh.checked_step(step=self.t, hyper=HP, rank_grads=self.grads, grad_base=sh.local_base,
-                                         divisor=self.divisor, max_norm=1.0, param16=self.p16,
+                                         divisor=self.divisor, max_norm=self.max_norm, param16=self.p16,
                                          param_base=self.param_base, grid_blocks=self.grid, events=timing)
             if inject:
                 self.grads[5][12345] = saved[0]
@@ -418,15 +501,18 @@ def cpu_baseline(w: Workload, seconds: float):
     lo, hi = ranges[0][0], ranges[-1][1]
     lb = lo & ~7
     seed = cfg
-    idx = synth.arange(lb, hi)
+
+    def gen(key, start, stop, dist, scale, code):  # inputs on all host cores (untimed)
+        return synth.host_values(key, start, stop - start, dist, scale, code)
+
     gcode = {2: synth.F16, 3: synth.BF16, 4: synth.F16, 5: synth.F32}[cfg]
     scale = w.grad_scale if cfg != 5 else 1e-3
     micro = None  # the per-step microstep work timed with the owner step (config 5)
     if w.schedule == "per-backward":
         # each of the eight microsteps reduces the 16 ranks' owned values into the owner's
         # accumulator (timed below; the eight microsteps reuse one microstep's values)
-        rows = [synth.values(synth.stream_key(seed, synth.STREAM_MICRO, r, 0), synth.arange(lo, hi),
-                             synth.DIST_NORMAL, 1e-3, synth.BF16) for r in range(w.R)]
+        rows = [gen(synth.stream_key(seed, synth.STREAM_MICRO, r, 0), lo, hi, synth.DIST_NORMAL, 1e-3, synth.BF16)
+                for r in range(w.R)]
         acc = np.zeros(hi - lo, dtype=np.float32)
 
         def micro():
@@ -440,8 +526,8 @@ def cpu_baseline(w: Workload, seconds: float):
         for r in range(w.R):
             acc_r = np.zeros(hi - lb, dtype=np.float32)
             for k in range(8):
-                g = synth.values(synth.stream_key(seed, synth.STREAM_MICRO, r, k), idx, synth.DIST_NORMAL,
-                                 1e-3, synth.BF16)
+                g = gen(synth.stream_key(seed, synth.STREAM_MICRO, r, k), lb, hi, synth.DIST_NORMAL, 1e-3,
+                        synth.BF16)
                 oracle.accumulate(g, synth.BF16, acc_r, first=(k == 0))
             grads.append(acc_r)
         # the local rank's eight microsteps over its whole flat buffer, which is
@@ -449,17 +535,16 @@ def cpu_baseline(w: Workload, seconds: float):
         # microsteps reuse one microstep's values)
         flat_per_owned = sh.padded_total / sh.n_real
         m = int(round((hi - lb) * flat_per_owned))
-        gm = synth.values(synth.stream_key(seed, synth.STREAM_MICRO, sh.owner, 0), synth.arange(0, m),
-                          synth.DIST_NORMAL, 1e-3, synth.BF16)
+        gm = gen(synth.stream_key(seed, synth.STREAM_MICRO, sh.owner, 0), 0, m, synth.DIST_NORMAL, 1e-3, synth.BF16)
         acc_local = np.zeros(m, dtype=np.float32)
 
         def micro():
             for k in range(8):
                 oracle.accumulate(gm, synth.BF16, acc_local, first=(k == 0))
     else:
-        grads = [synth.values(synth.stream_key(seed, synth.STREAM_GRAD, r), idx, synth.DIST_NORMAL,
-                              scale, gcode) for r in range(w.R)]
-    mk = lambda st, dist, s: synth.values_f32(synth.stream_key(seed, st, 0), idx, dist, s)
+        grads = [gen(synth.stream_key(seed, synth.STREAM_GRAD, r), lb, hi, synth.DIST_NORMAL, scale, gcode)
+                 for r in range(w.R)]
+    mk = lambda st, dist, s: gen(synth.stream_key(seed, st, 0), lb, hi, dist, s, synth.F32)
     w0 = mk(synth.STREAM_MASTER, synth.DIST_NORMAL, 0.02)
     m0 = mk(synth.STREAM_EXP_AVG, synth.DIST_NORMAL, 5e-4)
     v0 = mk(synth.STREAM_EXP_AVG_SQ, synth.DIST_SQUARE, 1e-4)
@@ -502,7 +587,11 @@ def cpu_baseline(w: Workload, seconds: float):
                 f"({flat_per_owned:.1f} per owned element), then reduce + AdamW + cast")
     else:
         what = "reduce + AdamW + cast"
-    return {"value": done / el, "unit": "params/s", "cores": oracle.num_threads(), "kind": "oracle",
+    rate = done / el
+    # the same algorithmic bytes per updated parameter as the GPU's updating step
+    per_param = w.step_bytes(False) / sh.n_real
+    return {"value": rate, "unit": "params/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "gbps": round(rate * per_param / 1e9, 3), "bytes_per_param": round(per_param, 3),
             "sample": f"first {n_real} real elements of the owner's shard, {reps} oracle step(s) "
                       f"({what}; inputs pre-generated)"}
 
@@ -775,7 +864,8 @@ def main():
     else:
         kname = {2: "adam_step_f16_f16", 3: "adam_step_bf16_bf16", 4: "reduce_check_f16_r64",
                  5: "accumulate_bf16"}[args.config]
-    ceil = None if args.no_ceiling else ceilings(kname)  # before the workload takes its memory
+    # before the workload takes its memory
+    ceil = None if args.no_ceiling else ceilings(kname, dominant_elements(args))
     if args.calibrate_copy:
         # a plain copy of known size: 2^28 fp32 read + 2^28 fp32 written per launch
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -846,7 +936,9 @@ def main():
         line["step_ms_update"] = step_stats([t for t, ok in zip(step_ms, launched) if ok])
         line["step_ms_overflow"] = step_stats([t for t, ok in zip(step_ms, launched) if not ok])
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        cpu["gpu_speedup"] = round(value / cpu["value"], 1)  # the GPU's params/s over the oracle's
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

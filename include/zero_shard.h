@@ -77,8 +77,10 @@ const char *zero_last_error(void);
  * when R exceeds P.  The pages do not give the padding; here every tensor,
  * the last included, is padded up to a multiple of `align_elems` elements
  * (tensor k starts at the sum of the padded sizes before it) and ownership is
- * taken over the padded total P.  Padding is owned but never read or written
- * by the device calls.
+ * taken over the padded total P.  Padding is owned, but the fused step and
+ * the copies never read or write it (they walk the chunk table); the flat
+ * reduce works on a flat range and treats padding like any other element,
+ * so rank gradient buffers hold zeros there (no parameter, no gradient).
  *
  * numel[n_tensors]          in : element count of each tensor, all > 0
  * ranks, align_elems        in : R >= 1, alignment in elements >= 1
@@ -187,7 +189,10 @@ int zero_state_bytes(uint64_t params, uint64_t ranks, uint32_t param_bytes, uint
  * The order is fixed, so results are identical run to run and bit-exact
  * against a sequential fp32 loop.  A loss scale is folded into `divisor`
  * (e.g. R * 65536).  R = 1, divisor = 1, accumulate = 1 is fp32 gradient
- * accumulation (acc += g) of one microstep.
+ * accumulation (acc += g) of one microstep.  The range may span the padding
+ * between tensors; it is reduced like real elements, so with zeros in the
+ * rank buffers' padding the check below equals the check over the real
+ * elements alone.
  *
  * rank_grads  host array [R] of device pointers; buffer r holds at least
  *             begin + n - grad_base elements of `grad_dtype` (F16, BF16, F32)
@@ -244,6 +249,31 @@ int zero_grad_check(const float *g, uint64_t n, int32_t *d_overflow, double *d_s
  * Errors: EINVAL for a negative or non-finite sumsq, max_norm <= 0, eps < 0.
  * -------------------------------------------------------------------------- */
 int zero_clip_coef(double sumsq, double max_norm, double eps, float *coef);
+
+/* ----------------------------------------------------------------------------
+ * zero_step_decision -- the host half of an overflow-checked, clipped step
+ * over several owners.
+ *
+ * The pages give neither the overflow skip nor the clip (see zero_clip_coef
+ * for the clip's form).  Every owner checks only its own slice, so the
+ * decision needs all of them: the step is skipped when any owner's flag is
+ * set; otherwise the global squared norm is the sum of the owners' partials,
+ * added in owner order in fp64, and the clip factor follows from it.  Every
+ * owner then takes the same decision and the same factor, which is what the
+ * unsharded step would do.  With one owner the partial is the whole norm.
+ *
+ * overflow[n_owners], sumsq[n_owners]  in : host arrays, one entry per owner
+ *                                           (what zero_reduce_owned's check or
+ *                                           zero_grad_check left on the device)
+ * max_norm, eps                        in : as for zero_clip_coef
+ * update                               out: 1 to apply the step, 0 to skip it
+ *                                           (the step count then stays)
+ * coef                                 out: the clip factor (0 when skipped)
+ * Errors: EINVAL for NULL pointers, n_owners == 0, a negative or non-finite
+ *         partial (only looked at when no flag is set), or bad max_norm / eps.
+ * -------------------------------------------------------------------------- */
+int zero_step_decision(const int32_t *overflow, const double *sumsq, uint32_t n_owners,
+                       double max_norm, double eps, int32_t *update, float *coef);
 
 /* ----------------------------------------------------------------------------
  * zero_chunk_groups -- packs runs of short chunks into groups that one block
@@ -464,27 +494,35 @@ int zero_copy_spans(const zero_copy_span *spans, uint64_t n_spans, const void *c
 /* ----------------------------------------------------------------------------
  * zero_stream_probe -- the bandwidth probe against which the optimizer kernels
  * are measured (no part of the optimizer step; the pages define no such
- * operation).  Every destination receives the bytewise XOR of all sources:
- * dsts[d][i] = srcs[0][i] ^ ... ^ srcs[n_src-1][i] for i < bytes (all zero
- * bytes without sources), streamed with 16-byte loads and stores, one block
- * per 256-vector piece, so one launch moves (n_src + n_dst) * bytes bytes of
- * HBM traffic.  One source and one destination is a plain copy; no
- * destinations reads only, no sources writes only.
+ * operation).  Every destination receives the bytewise XOR of all sources,
+ * streamed with 16-byte loads and stores, one block per 256-thread piece.
+ * A stream's width w (1 or 2) is the number of consecutive 16-byte vectors
+ * each thread touches: width 1 is how the kernels stream 16-bit data (8
+ * elements, 16 bytes per thread), width 2 how they stream fp32 data (8
+ * elements, 32 bytes), so a probe can copy a kernel's exact stream structure.
+ * With `bytes` per width unit, thread i of the grid (i < bytes / 16) reads
+ * vectors [w i, w i + w) of every source, XORs them all into one vector and
+ * writes it to vectors [w i, w i + w) of every destination; a stream of width
+ * w spans w * bytes bytes, and one launch moves the sum of all of them.  One
+ * source and one destination of width 1 is a plain copy; no destinations
+ * reads only, no sources writes zeros.
  * srcs[n_src], dsts[n_dst]  host arrays of device pointers, each 16-byte
  *                           aligned; n_src, n_dst <= ZERO_MAX_PROBE_STREAMS,
  *                           not both 0 (an empty array may be NULL)
- * bytes                     bytes per stream, a multiple of 16 (0: no launch)
+ * src_widths, dst_widths    host arrays of 1 or 2 per stream, or NULL (all 1)
+ * bytes                     bytes per width unit, a multiple of 16 (0: no launch)
  * order                     0: block b takes piece b (blocks are dealt to the
  *                           8 XCDs in turn); 1: each XCD takes one contiguous
  *                           run of pieces.  Which is faster depends on the
  *                           number of streams.
  * A destination that overlaps a source or another destination gives
  * unspecified contents (no fault: every access stays inside the streams).
- * Errors: EINVAL (stream counts, NULL or misaligned pointers, bytes not a
- * multiple of 16, order not 0 or 1); EHIP.
+ * Errors: EINVAL (stream counts, NULL or misaligned pointers, a width other
+ * than 1 or 2, bytes not a multiple of 16, order not 0 or 1); EHIP.
  * -------------------------------------------------------------------------- */
-int zero_stream_probe(const void *const *srcs, uint32_t n_src, void *const *dsts, uint32_t n_dst,
-                      uint64_t bytes, int order, hipStream_t stream);
+int zero_stream_probe(const void *const *srcs, const uint8_t *src_widths, uint32_t n_src,
+                      void *const *dsts, const uint8_t *dst_widths, uint32_t n_dst, uint64_t bytes,
+                      int order, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -97,7 +97,8 @@ double oracle_f16_value(uint16_t b) { return decode16(b, 10, 15); }
 double oracle_bf16_value(uint16_t b) { return decode16(b, 7, 127); }
 
 void oracle_encode16(const float *x, uint64_t n, int dtype, uint16_t *out) {
-  for (uint64_t i = 0; i < n; ++i)
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < (int64_t)n; ++i)
     out[i] = dtype == OR_F16 ? oracle_f32_to_f16(x[i]) : oracle_f32_to_bf16(x[i]);
 }
 

@@ -216,6 +216,7 @@ def build(verbose: bool = False) -> str:
         "hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Xclang", "-target-feature", "-Xclang", "-fma-mix-insts",
         src, "-o", tmp,
     ]
     res = subprocess.run(cmd, capture_output=True, text=True)

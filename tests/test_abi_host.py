@@ -214,18 +214,23 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
         need = zs.check_workspace_bytes(n)
         assert L.zero_grad_check(ct.c_void_p(0x20000), n, ov, ss, ws, need - 1, None) == zs.ZERO_EINVAL
         assert b"workspace" in L.zero_last_error()
-    # bandwidth probe: stream counts, byte size, NULL and misaligned pointers
+    # bandwidth probe: stream counts, byte size, widths, NULL and misaligned pointers
     two = (ct.c_void_p * 2)(0x1000, 0x2000)
-    assert L.zero_stream_probe(two, 0, two, 0, 64, 0, None) == zs.ZERO_EINVAL
-    assert L.zero_stream_probe(two, 65, two, 1, 64, 0, None) == zs.ZERO_EINVAL
-    assert L.zero_stream_probe(two, 1, two, 65, 64, 0, None) == zs.ZERO_EINVAL
-    assert L.zero_stream_probe(two, 1, two, 1, 24, 0, None) == zs.ZERO_EINVAL
-    assert L.zero_stream_probe(None, 1, two, 1, 64, 0, None) == zs.ZERO_EINVAL
-    assert L.zero_stream_probe(two, 1, None, 1, 64, 0, None) == zs.ZERO_EINVAL
-    assert L.zero_stream_probe(bad, 1, two, 1, 64, 0, None) == zs.ZERO_EINVAL
-    assert L.zero_stream_probe((ct.c_void_p * 1)(0), 1, two, 1, 64, 0, None) == zs.ZERO_EINVAL
-    assert L.zero_stream_probe(two, 1, two, 1, 0, 0, None) == zs.ZERO_OK  # nothing to move
-    assert L.zero_stream_probe(two, 1, two, 1, 64, 2, None) == zs.ZERO_EINVAL  # order 0 or 1
+    P = L.zero_stream_probe
+    assert P(two, None, 0, two, None, 0, 64, 0, None) == zs.ZERO_EINVAL
+    assert P(two, None, 65, two, None, 1, 64, 0, None) == zs.ZERO_EINVAL
+    assert P(two, None, 1, two, None, 65, 64, 0, None) == zs.ZERO_EINVAL
+    assert P(two, None, 1, two, None, 1, 24, 0, None) == zs.ZERO_EINVAL
+    assert P(None, None, 1, two, None, 1, 64, 0, None) == zs.ZERO_EINVAL
+    assert P(two, None, 1, None, None, 1, 64, 0, None) == zs.ZERO_EINVAL
+    assert P(bad, None, 1, two, None, 1, 64, 0, None) == zs.ZERO_EINVAL
+    assert P((ct.c_void_p * 1)(0), None, 1, two, None, 1, 64, 0, None) == zs.ZERO_EINVAL
+    assert P(two, None, 1, two, None, 1, 0, 0, None) == zs.ZERO_OK  # nothing to move
+    assert P(two, None, 1, two, None, 1, 64, 2, None) == zs.ZERO_EINVAL  # order 0 or 1
+    w3, w0 = (ct.c_uint8 * 2)(3, 1), (ct.c_uint8 * 2)(1, 0)
+    assert P(two, w3, 1, two, None, 1, 64, 0, None) == zs.ZERO_EINVAL  # widths 1 or 2
+    assert P(two, None, 1, two, w0, 2, 64, 0, None) == zs.ZERO_EINVAL
+    assert b"width" in L.zero_last_error()
 
 
 def test_check_workspace_grows_with_the_block_count():
@@ -394,3 +399,22 @@ def test_piece_orders_are_bijections(tmp_path):
     assert res.returncode == 0, res.stderr[-3000:]
     run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert run.returncode == 0 and "clean" in run.stdout, run.stdout[-2000:]
+
+
+def test_device_code_has_no_mixed_precision_fma():
+    """The library's build flags keep the fp16 write-back a rounding of the stored
+    fp32 master weight: without them the compiler folds the fp16 conversion of
+    an fma result into v_fma_mix (one rounding of the exact a*b+c to fp16).
+    The gfx950 assembly of the step kernels, built with those flags, holds no
+    such instruction (and does hold the plain conversions)."""
+    from zero_sharded_optimizer_owned_amd.build import CSRC, HIPCC_FLAGS, INCLUDE
+
+    if shutil.which("hipcc") is None:
+        pytest.skip("no hipcc")
+    flags = [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+    res = subprocess.run(["hipcc", *flags, "-I", INCLUDE, "--cuda-device-only", "-S",
+                          os.path.join(CSRC, "step.hip"), "-o", "-"], capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stderr[-2000:]
+    asm = res.stdout
+    assert "v_fma_mix" not in asm and "v_mad_mix" not in asm
+    assert "v_cvt_f16_f32" in asm

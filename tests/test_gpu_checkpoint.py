@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import F16, F32, assert_bits_equal, from_dev, gen, to_dev
+from helpers import F16, F32, assert_bits_equal, from_dev, gen, shard_ranges, to_dev
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -48,13 +48,16 @@ def test_export_import_matches_oracle(numels, R, A, max_chunk):
     dense = torch.full((sum(numels),), float("nan"), device=DEV)
     for sh, a in zip(shards, arrays):
         sh.to_dense(to_dev(a, F32), dense)
-    owners = [(sh.begin, sh.end) for sh in shards]
-    want = oracle.consolidate(numels, list(shards[0].offsets), owners, arrays, [sh.local_base for sh in shards])
+    off, _, owners = oracle.layout(numels, R, A)  # expected layout; the shards must agree with it
+    for sh in shards:
+        shard_ranges(sh)
+        assert [int(x) for x in sh.dense_offsets] == oracle.dense_offsets(numels)
+    want = oracle.consolidate(numels, off, owners, arrays, [b & ~7 for b, _ in owners])
     assert_bits_equal(from_dev(dense), want, "export")
     for sh in shards:
         back = torch.full((max(8, sh.local_size),), -1.0, device=DEV)
         sh.from_dense(dense, back)
-        ref = oracle.distribute(numels, list(sh.offsets), sh.begin, sh.end, want,
+        ref = oracle.distribute(numels, off, sh.begin, sh.end, want,
                                 np.full(max(8, sh.local_size), -1.0, dtype=np.float32), sh.local_base)
         assert_bits_equal(from_dev(back), ref, "import")
 

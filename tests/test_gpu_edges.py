@@ -21,7 +21,7 @@ import numpy as np
 import pytest
 
 import oracle
-from helpers import BF16, F16, F32, assert_bits_equal, from_dev, to_dev
+from helpers import BF16, F16, F32, assert_bits_equal, checked_layout, from_dev, to_dev
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -86,7 +86,7 @@ def test_write_back_encodes_the_master_weight_exactly(pcode, grouped):
     print(f"write-back {pcode} grouped={grouped} n={n}", flush=True)
     # two tensors, the second short and padded, so that chunks, vectors and scalar ends all occur
     numels = [n - 13, 13]
-    off, total, b, e = zs.zero_shard_layout(numels, 1, 8)
+    off, total, b, e = checked_layout(numels, 1, 8)
     begin, end = int(b[0]), int(e[0])
     flat_w = np.zeros(end, dtype=np.float32)
     flat_w[:n - 13] = w[:n - 13]
@@ -181,11 +181,11 @@ def test_fused_step_at_extreme_steps_and_betas(step, beta1, beta2):
     1e-7 abs, 16-bit copy within 1 ulp), where the host's fp64 bias corrections
     are tiny, exactly one, or the betas are zero."""
     import synth
-    from helpers import assert_p16_within_ulp, assert_state_close, gen
+    from helpers import assert_copy_of_master, assert_state_close, gen
 
     print(f"hyper edges step={step} beta1={beta1} beta2={beta2}", flush=True)
     numels, R, A, owner = [1000, 37, 5003, 1, 777], 3, 64, 1
-    off, total, b, e = zs.zero_shard_layout(numels, R, A)
+    off, total, b, e = checked_layout(numels, R, A)
     begin, end = int(b[owner]), int(e[owner])
     lb = begin & ~7
     size = end - lb
@@ -207,7 +207,4 @@ def test_fused_step_at_extreme_steps_and_betas(step, beta1, beta2):
     assert_state_close(from_dev(dw), w, "w")
     assert_state_close(from_dev(dm), m, "m")
     assert_state_close(from_dev(dv), v, "v")
-    real = np.zeros(total, dtype=bool)
-    for s, t in ranges:
-        real[s:t] = True
-    assert_p16_within_ulp(from_dev(dp)[real], p_host[real], "p16")
+    assert_copy_of_master(from_dev(dp), p_host, from_dev(dw), w, lb, ranges, F16, "p16")

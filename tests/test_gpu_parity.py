@@ -13,7 +13,8 @@ import pytest
 
 import oracle
 import synth
-from helpers import (BF16, F16, F32, assert_bits_equal, assert_p16_within_ulp, assert_state_close,
+from helpers import (BF16, F16, F32, assert_bits_equal, assert_chunks_cover, assert_copy_of_master, assert_state_close,
+                     checked_layout, shard_ranges,
                      from_dev, gen, to_dev)
 
 torch = pytest.importorskip("torch")
@@ -196,7 +197,7 @@ LAYOUTS = {
 
 
 def _owner_inputs(numels, R, A, owner, gcode, seed):
-    off, total, b, e = zs.zero_shard_layout(numels, R, A)
+    off, total, b, e = checked_layout(numels, R, A)
     begin, end = int(b[owner]), int(e[owner])
     lb = begin & ~7
     grads = _rank_inputs(gcode, R, total, seed=seed)
@@ -228,6 +229,7 @@ def test_adam_step_matches_oracle(layout, gcode, pcode, max_chunk, grouped):
         dp = to_dev(p16_host, pcode) if pcode else None
         ow, om, ov_ = w.copy(), m.copy(), v.copy()
         ranges = oracle.real_ranges(numels, list(off), begin, end)
+        assert_chunks_cover(chunks, ranges, f"{layout} owner {owner}")
         for t in (11, 12, 13):  # independent trajectories, three steps
             zs.zero_adam_step(chunks_dev=dchunks, n_chunks=chunks.size, begin=begin, end=end,
                               master=dw, exp_avg=dm, exp_avg_sq=dv, local_base=lb, step=t,
@@ -245,7 +247,7 @@ def test_adam_step_matches_oracle(layout, gcode, pcode, max_chunk, grouped):
                 for s, e_ in ranges:
                     real[s:e_] = True
                 assert np.all(got[~real] == sentinel), what + ": padding or foreign elements written"
-                assert_p16_within_ulp(got[real], p16_host[real], what + " p16")
+                assert_copy_of_master(got, p16_host, from_dev(dw), ow, lb, ranges, pcode, what + " p16")
 
 
 def test_group_tables_give_the_same_bits():
@@ -253,7 +255,7 @@ def test_group_tables_give_the_same_bits():
     chunks (more chunks and more work units than one block has threads) and a
     small grid that strides over the groups: identical bits every way."""
     numels, R, A = [1 + (53 * k) % 120 for k in range(700)], 2, 64
-    off, total, b, e = zs.zero_shard_layout(numels, R, A)
+    off, total, b, e = checked_layout(numels, R, A)
     begin, end = int(b[1]), int(e[1])
     lb = begin & ~7
     grads = [to_dev(g, F16) for g in _rank_inputs(F16, R, total, seed=12)]
@@ -329,7 +331,7 @@ def test_two_pass_with_clip_matches_oracle_and_fused():
     assert_state_close(from_dev(dw), ow, "w")
     assert_state_close(from_dev(dm), om, "m")
     assert_state_close(from_dev(dv), ovv, "v")
-    assert_p16_within_ulp(from_dev(dp), p_or, "p16")
+    assert_copy_of_master(from_dev(dp), p_or, from_dev(dw), ow, lb, ranges, F16, "p16")
     # the fused single pass gives the same bits as reduce-then-step with coef 1
     fw, fm, fv = to_dev(w, F32), to_dev(m, F32), to_dev(v, F32)
     tw, tm, tv = to_dev(w, F32), to_dev(m, F32), to_dev(v, F32)
@@ -352,7 +354,7 @@ def test_fused_step_every_rank_path(code, R):
     layout has two owners; the rank count only sets how many buffers are
     summed."""
     numels, A = [1000, 37, 5003, 1, 64, 777], 64
-    off, total, b, e = zs.zero_shard_layout(numels, 2, A)
+    off, total, b, e = checked_layout(numels, 2, A)
     begin, end = int(b[1]), int(e[1])
     lb = begin & ~7
     grads = _rank_inputs(code, R, total, seed=50 + R)
@@ -377,7 +379,7 @@ def test_fused_step_every_rank_path(code, R):
     assert_state_close(from_dev(dw), ow, what + " w")
     assert_state_close(from_dev(dm), om, what + " m")
     assert_state_close(from_dev(dv), ovv, what + " v")
-    assert_p16_within_ulp(from_dev(dp), p_or, what + " p16")
+    assert_copy_of_master(from_dev(dp), p_or, from_dev(dw), ow, lb, ranges, pcode, what + " p16")
     # reduce-then-step: the flat reduce over the owner range, then AdamW from it
     g_dev = torch.zeros(size, dtype=torch.float32, device=DEV)
     zs.zero_reduce_owned(dgr, begin, end - begin, float(R), g_dev, out_base=lb)
@@ -428,7 +430,7 @@ def test_checked_step_skips_clips_and_updates():
     assert want_coef < 0.5 and abs(coef - want_coef) <= 1e-6 * want_coef
     g_loc = np.zeros(sh.local_size, dtype=np.float32)
     g_loc[begin - lb:] = g_or
-    ranges = oracle.real_ranges(numels, list(sh.offsets), begin, end)
+    ranges = shard_ranges(sh)
     ow, om, ov_ = w.copy(), m.copy(), v.copy()
     p_or = np.zeros(total, dtype=np.uint16)
     oracle.owner_step(ranges, oracle.hyper(step=3, clip_coef=coef, **HP), ow, om, ov_, lb, reduced_g=g_loc,
@@ -436,7 +438,7 @@ def test_checked_step_skips_clips_and_updates():
     assert_state_close(from_dev(sh.master)[:sh.local_size], ow, "w")
     assert_state_close(from_dev(sh.exp_avg)[:sh.local_size], om, "m")
     assert_state_close(from_dev(sh.exp_avg_sq)[:sh.local_size], ov_, "v")
-    assert_p16_within_ulp(from_dev(dp), p_or, "p16")
+    assert_copy_of_master(from_dev(dp), p_or, from_dev(sh.master), ow, lb, ranges, F16, "p16")
     # an inf in one rank: the step is skipped and no state or 16-bit value changes
     before = [from_dev(x).copy() for x in (sh.master, sh.exp_avg, sh.exp_avg_sq, dp)]
     dgr[2][begin + 5] = float("inf")
@@ -449,6 +451,81 @@ def test_checked_step_skips_clips_and_updates():
     assert empty.begin == empty.end
     empty.alloc_state()
     assert empty.checked_step(step=1, hyper=HP, rank_grads=[to_dev(np.zeros(8, np.float32), F32)]) == (True, 1.0)
+
+
+@pytest.mark.parametrize("numels,R,A,scale", [([3000, 77, 20_001, 5, 9000], 5, 64, 0.5), ([3, 2], 9, 1, 40.0),
+                                               ([40, 7, 1000], 4, 8, 2.0)])
+def test_checked_step_over_every_owner_is_the_unsharded_clip_and_skip(numels, R, A, scale):
+    """Every owner of a layout (empty owners included) reduces and checks its own
+    slice; the host combines the flags and partial norms (zero_step_decision)
+    and every owner applies the same decision.  The result is the oracle's
+    unsharded step: one overflow flag and one clip factor from the whole
+    gradient.  Then an inf in one owner's slice skips every owner's step."""
+    off, total, owners = oracle.layout(numels, R, A)
+    shards = [zs.OwnerShard(numels, R, r, align=A, max_chunk=256, device=DEV) for r in range(R)]
+    ranges = [shard_ranges(sh) for sh in shards]
+    grads = _rank_inputs(F16, R, total, seed=31, scale=scale)  # the whole norm is far above 1
+    # the rank buffers hold zeros in the padding (no parameter lives there): the
+    # checked reduce runs over each owner's flat range, padding included
+    pad = np.ones(total, dtype=bool)
+    for rr in ranges:
+        for b, e in rr:
+            pad[b:e] = False
+    for g in grads:
+        g[pad] = 0
+    dgr = [to_dev(g, F16) for g in grads]
+    w = gen(31, synth.STREAM_MASTER, total + 8, synth.DIST_NORMAL, 0.02, F32)
+    m = gen(31, synth.STREAM_EXP_AVG, total + 8, synth.DIST_NORMAL, 5e-4, F32)
+    v = gen(31, synth.STREAM_EXP_AVG_SQ, total + 8, synth.DIST_SQUARE, 1e-4, F32)
+    for sh in shards:
+        sh.alloc_state()
+        for dst, src in ((sh.master, w), (sh.exp_avg, m), (sh.exp_avg_sq, v)):
+            dst[:sh.local_size].copy_(to_dev(src[sh.local_base:sh.end], F32))
+    dp = torch.zeros(total, dtype=torch.float16, device=DEV)
+
+    def run(step):
+        parts = [sh.reduce_and_check(rank_grads=dgr, divisor=float(R)) for sh in shards]
+        updated, coef = zs.zero_step_decision([f for f, _ in parts], [s for _, s in parts], 1.0)
+        if updated:
+            for sh in shards:
+                sh.apply_update(step=step, hyper=HP, coef=coef, param16=dp)
+        return updated, coef
+
+    updated, coef = run(3)
+    # the oracle's unsharded step: the whole gradient's flag and norm
+    real = [rg for rr in ranges for rg in rr]
+    g_all = np.zeros(total, dtype=np.float32)
+    for b, e in real:
+        g_all[b:e] = oracle.reduce([g[b:e] for g in grads], F16, float(R))
+    flag, sumsq = oracle.grad_check(np.concatenate([g_all[b:e] for b, e in real]))
+    assert flag == 0 and updated
+    want_coef = oracle.clip_coef(sumsq)
+    assert want_coef < 0.5 and abs(coef - want_coef) <= 1e-6 * want_coef
+    ow, om, ov_ = w.copy(), m.copy(), v.copy()
+    p_or = np.zeros(total, dtype=np.uint16)
+    oracle.owner_step(real, oracle.hyper(step=3, clip_coef=coef, **HP), ow, om, ov_, 0, reduced_g=g_all,
+                      p16=p_or, pdtype=F16)
+    for r, sh in enumerate(shards):
+        b, e, lb = sh.begin, sh.end, sh.local_base
+        for got, want, nm in ((sh.master, ow, "w"), (sh.exp_avg, om, "m"), (sh.exp_avg_sq, ov_, "v")):
+            assert_state_close(from_dev(got)[b - lb:e - lb], want[b:e], f"owner {r} {nm}")
+    gw = w.copy()  # the kernels' master weights, flat-indexed
+    for sh in shards:
+        gw[sh.begin:sh.end] = from_dev(sh.master)[sh.begin - sh.local_base:sh.end - sh.local_base]
+    assert_copy_of_master(from_dev(dp), p_or, gw, ow, 0, real, F16, "p16")
+    # one owner's slice holds an inf: every owner skips, nothing changes anywhere
+    r_bad = max(range(R), key=lambda r: shards[r].end - shards[r].begin)
+    before = [[from_dev(x).copy() for x in (sh.master, sh.exp_avg, sh.exp_avg_sq)] for sh in shards]
+    p_before = from_dev(dp).copy()
+    dgr[1][ranges[r_bad][0][0]] = float("inf")  # the owner's first real element
+    assert run(4) == (False, None)
+    for sh, old in zip(shards, before):
+        for a, x in zip(old, (sh.master, sh.exp_avg, sh.exp_avg_sq)):
+            assert np.array_equal(a.view(np.uint32), from_dev(x).view(np.uint32))
+    assert np.array_equal(p_before, from_dev(dp))
+    # the owners without the inf saw no overflow of their own: the decision is global
+    own_flags = [sh.reduce_and_check(rank_grads=dgr, divisor=float(R))[0] for sh in shards]
+    assert own_flags[r_bad] == 1 and sum(own_flags) == 1
 
 
 def test_no_op_cases_leave_memory_untouched():
@@ -543,7 +620,7 @@ def test_per_backward_schedule_matches_oracle():
     """Four microsteps: each reduces the ranks' owned slices and adds the mean to the
     owner's fp32 accumulator; AdamW runs once from it at the boundary."""
     numels, R, A, K = [3000, 77, 20_001, 5], 4, 64, 4
-    off, total, b, e = zs.zero_shard_layout(numels, R, A)
+    off, total, b, e = checked_layout(numels, R, A)
     owner = 2
     begin, end = int(b[owner]), int(e[owner])
     lb = begin & ~7
@@ -569,12 +646,12 @@ def test_per_backward_schedule_matches_oracle():
                       master=dw, exp_avg=dm, exp_avg_sq=dv, local_base=lb, step=7, reduced_g=acc_dev,
                       param16=dp, **HP)
     p_or = np.zeros(total, dtype=np.uint16)
-    oracle.owner_step(oracle.real_ranges(numels, list(off), begin, end), oracle.hyper(step=7, **HP),
-                      w, m, v, lb, reduced_g=acc, p16=p_or, pdtype=BF16)
+    ranges = oracle.real_ranges(numels, list(off), begin, end)
+    oracle.owner_step(ranges, oracle.hyper(step=7, **HP), w, m, v, lb, reduced_g=acc, p16=p_or, pdtype=BF16)
     assert_state_close(from_dev(dw), w, "w")
     assert_state_close(from_dev(dm), m, "m")
     assert_state_close(from_dev(dv), v, "v")
-    assert_p16_within_ulp(from_dev(dp), p_or, "p16")
+    assert_copy_of_master(from_dev(dp), p_or, from_dev(dw), w, lb, ranges, BF16, "p16")
 
 
 # ---------------------------------------------------------------- launch-shape independence
@@ -604,7 +681,7 @@ def test_fused_step_is_deterministic_and_independent_of_grid_and_chunking():
 
 def test_chunks_outside_the_owner_range_are_ignored():
     numels, R, A, owner = [5000, 3000], 3, 8, 1
-    off, total, b, e = zs.zero_shard_layout(numels, R, A)
+    off, total, b, e = checked_layout(numels, R, A)
     begin, end = int(b[owner]), int(e[owner])
     good = zs.zero_chunk_table(numels, off, begin, end, 512)
     ref = _fused_once(numels, R, A, owner, 512, 0)

@@ -61,3 +61,29 @@ def test_probe_rejects_mismatched_sizes():
     c = torch.zeros(68, dtype=torch.int32, device="cuda")
     with pytest.raises(zs.ZeroShardError):
         zs.zero_stream_probe([b[1:65]], [c[1:65]])  # 16-byte alignment
+
+
+@pytest.mark.parametrize("src_w,dst_w,n_vec", [([1, 2], [2], 70_001), ([1] * 8 + [2] * 3, [2, 2, 2, 1], 9_999),
+                                               ([2] * 4, [2, 2, 2, 1], 256 * 3 + 7), ([1] * 64, [2], 517)])
+def test_probe_with_stream_widths(src_w, dst_w, n_vec):
+    """Streams of width 2 hand each thread two consecutive 16-byte vectors: thread i
+    XORs vectors [w i, w i + w) of every source (both vectors of a wide source
+    into the same lanes) and writes the result to both vectors of a wide
+    destination.  Expected values are built with numpy from the host copies."""
+    rng = np.random.default_rng(len(src_w) * 100 + n_vec)
+    host = [rng.integers(0, 2 ** 32, size=(n_vec, w, 4), dtype=np.uint32) for w in src_w]
+    srcs = [torch.from_numpy(h.reshape(-1).view(np.int32)).to("cuda") for h in host]
+    acc = np.zeros((n_vec, 4), dtype=np.uint32)
+    for h in host:
+        acc ^= np.bitwise_xor.reduce(h, axis=1)
+    dsts = [torch.full((4 * n_vec * w + 8,), -7, dtype=torch.int32, device="cuda") for w in dst_w]
+    zs.zero_stream_probe(srcs, [d[:4 * n_vec * w] for d, w in zip(dsts, dst_w)], 1, src_widths=src_w,
+                         dst_widths=dst_w)
+    torch.cuda.synchronize()
+    for d, w in zip(dsts, dst_w):
+        got = d.cpu().numpy().view(np.uint32)
+        want = np.repeat(acc[:, None, :], w, axis=1).reshape(-1)
+        assert np.array_equal(got[:4 * n_vec * w], want)
+        assert np.all(got[4 * n_vec * w:].view(np.int32) == -7)
+    with pytest.raises(ValueError):
+        zs.zero_stream_probe(srcs[:1], [dsts[0][:4 * n_vec * dst_w[0]]], src_widths=[3], dst_widths=dst_w[:1])

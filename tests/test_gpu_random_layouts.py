@@ -18,7 +18,8 @@ import pytest
 
 import oracle
 import synth
-from helpers import BF16, F16, F32, assert_p16_within_ulp, assert_state_close, from_dev, gen, to_dev
+from helpers import (BF16, F16, F32, assert_chunks_cover, assert_copy_of_master, assert_state_close,
+                     checked_layout, from_dev, gen, shard_ranges, to_dev)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -62,7 +63,7 @@ def test_random_layout_step_matches_oracle(seed):
     c = _case(seed)
     print(f"case {seed}: {c}", flush=True)
     numels, R = c["sizes"], c["R"]
-    off, total, b, e = zs.zero_shard_layout(numels, R, c["A"])
+    off, total, b, e = checked_layout(numels, R, c["A"])
     begin, end = int(b[c["owner"]]), int(e[c["owner"]])
     lb = begin & ~7
     size = max(8, end - lb)
@@ -85,6 +86,7 @@ def test_random_layout_step_matches_oracle(seed):
                       step=c["step"], rank_grads=[to_dev(g, c["gcode"]) for g in grads], divisor=float(R),
                       param16=dp, clip_coef=c["clip"], **kw, **hp)
     ranges = oracle.real_ranges(numels, list(off), begin, end)
+    assert_chunks_cover(chunks, ranges, f"case {seed}")
     oracle.owner_step(ranges, oracle.hyper(step=c["step"], clip_coef=c["clip"], **hp), w, m, v, lb,
                       grads=grads, gdtype=c["gcode"], divisor=float(R),
                       p16=p_host if c["pcode"] else None, pdtype=c["pcode"])
@@ -97,7 +99,7 @@ def test_random_layout_step_matches_oracle(seed):
         for s, t in ranges:
             real[s:t] = True
         assert np.all(got[~real] == sentinel), f"case {seed}: padding or foreign elements written"
-        assert_p16_within_ulp(got[real], p_host[real], f"case {seed} p16")
+        assert_copy_of_master(got, p_host, from_dev(dw), w, lb, ranges, c["pcode"], f"case {seed} p16")
 
 
 @pytest.mark.parametrize("seed", range(30))
@@ -179,13 +181,16 @@ def test_random_export_import_matches_oracle(seed):
     dense = torch.full((sum(numels),), float("nan"), device=DEV)
     for sh, a in zip(shards, arrays):
         sh.to_dense(to_dev(a, F32), dense)
-    owners = [(sh.begin, sh.end) for sh in shards]
-    want = oracle.consolidate(numels, list(shards[0].offsets), owners, arrays, [sh.local_base for sh in shards])
+    off, _, owners = oracle.layout(numels, R, A)  # expected layout; the shards must agree with it
+    for sh in shards:
+        shard_ranges(sh)
+        assert [int(x) for x in sh.dense_offsets] == oracle.dense_offsets(numels)
+    want = oracle.consolidate(numels, off, owners, arrays, [b & ~7 for b, _ in owners])
     assert_bits_equal(from_dev(dense), want, f"case {seed} export")
     for sh in shards:
         back = torch.full((max(8, sh.local_size),), -1.0, device=DEV)
         sh.from_dense(dense, back)
-        ref = oracle.distribute(numels, list(sh.offsets), sh.begin, sh.end, want,
+        ref = oracle.distribute(numels, off, sh.begin, sh.end, want,
                                 np.full(max(8, sh.local_size), -1.0, dtype=np.float32), sh.local_base)
         assert_bits_equal(from_dev(back), ref, f"case {seed} import")
 

@@ -28,7 +28,7 @@ ZERO_NONE, ZERO_F16, ZERO_BF16, ZERO_F32 = 0, 1, 2, 3
 ZERO_MAX_RANKS = 256
 
 EXPORTED = ("zero_last_error", "zero_shard_layout", "zero_chunk_table", "zero_dense_offsets", "zero_state_bytes",
-            "zero_reduce_owned", "zero_grad_check", "zero_clip_coef", "zero_adam_step",
+            "zero_reduce_owned", "zero_grad_check", "zero_clip_coef", "zero_step_decision", "zero_adam_step",
             "zero_owner_to_dense", "zero_dense_to_owner", "zero3_storage", "zero3_gather_spans",
             "zero3_partition_spans", "zero_copy_spans", "zero_stream_probe",
             "zero_check_workspace_bytes", "zero_chunk_groups", "zero_span_groups")
@@ -83,6 +83,7 @@ def load(path: str):
     L.zero_reduce_owned.argtypes = [P, U32, I, U64, U64, U64, F, I, P, U64, P, P, P, ct.c_size_t, P]
     L.zero_grad_check.argtypes = [P, U64, P, P, P, ct.c_size_t, P]
     L.zero_clip_coef.argtypes = [D, D, D, ct.POINTER(F)]
+    L.zero_step_decision.argtypes = [P, P, U32, D, D, ct.POINTER(ct.c_int32), ct.POINTER(F)]
     L.zero_adam_step.argtypes = [ct.POINTER(AdamArgs), P]
     L.zero_owner_to_dense.argtypes = [P, U64, P, U64, U64, U64, P, P, U32, P, U64, P, U64, P]
     L.zero_dense_to_owner.argtypes = [P, U64, P, U64, U64, U64, P, P, U32, P, U64, P, U64, P]
@@ -91,7 +92,7 @@ def load(path: str):
     L.zero3_partition_spans.argtypes = [P, U32, U32, U32, U32, P, U64, P]
     L.zero_copy_spans.argtypes = [P, U64, P, P, U32, P, U64, U32, P, U64, P]
     L.zero_span_groups.argtypes = [P, U64, U32, U32, P, U64, P]
-    L.zero_stream_probe.argtypes = [P, U32, P, U32, U64, I, P]
+    L.zero_stream_probe.argtypes = [P, P, U32, P, P, U32, U64, I, P]
     L.zero_check_workspace_bytes.argtypes = [U64, P]
     L.zero_chunk_groups.argtypes = [P, U64, U32, P, U64, P]
     return L
@@ -187,6 +188,19 @@ def zero_clip_coef(sumsq: float, max_norm: float = 1.0, eps: float = 1e-6) -> fl
     c = ct.c_float()
     _check(lib().zero_clip_coef(sumsq, max_norm, eps, ct.byref(c)))
     return c.value
+
+
+def zero_step_decision(overflow: Sequence[int], sumsq: Sequence[float], max_norm: float = 1.0,
+                       eps: float = 1e-6):
+    """(update, clip factor) from every owner's (flag, squared-norm partial), in
+    owner order; the factor is None when the step is skipped."""
+    fl = np.ascontiguousarray(np.asarray(overflow, dtype=np.int32))
+    ss = np.ascontiguousarray(np.asarray(sumsq, dtype=np.float64))
+    if fl.size != ss.size:
+        raise ValueError("one flag and one partial per owner")
+    up, c = ct.c_int32(), ct.c_float()
+    _check(lib().zero_step_decision(_p(fl), _p(ss), fl.size, max_norm, eps, ct.byref(up), ct.byref(c)))
+    return (True, c.value) if up.value else (False, None)
 
 
 # ---------------------------------------------------------------- device calls
@@ -484,26 +498,33 @@ def zero_copy_spans(spans_dev, n_spans: int, srcs, dst, groups_dev=None, n_group
                                  dst.numel(), dst.element_size(), gptr, ng, _stream()))
 
 
-def zero_stream_probe(srcs, dsts, order: int = 0) -> None:
+def zero_stream_probe(srcs, dsts, order: int = 0, src_widths=None, dst_widths=None) -> None:
     """Bandwidth probe: every destination gets the bytewise XOR of all sources.
 
-    All tensors are contiguous device tensors of one byte size (a multiple of
-    16); one launch moves (len(srcs) + len(dsts)) * that many bytes.  No
-    destinations: reads only; no sources: writes zeros.  ``order`` 0 deals the
-    pieces to the XCDs in turn, 1 gives each XCD one contiguous run.
+    A stream of width w (1 or 2; default 1) is touched w 16-byte vectors per
+    thread, as the kernels stream 16-bit (w = 1) and fp32 (w = 2) data; every
+    stream's byte size is its width times one common unit (a multiple of 16).
+    No destinations: reads only; no sources: writes zeros.  ``order`` 0 deals
+    the pieces to the XCDs in turn, 1 gives each XCD one contiguous run.
     """
     if len(srcs) > ZERO_MAX_PROBE_STREAMS or len(dsts) > ZERO_MAX_PROBE_STREAMS or not (srcs or dsts):
         raise ValueError(f"at most {ZERO_MAX_PROBE_STREAMS} sources and destinations, not none of both")
-    first = (list(srcs) + list(dsts))[0]
-    nbytes = first.numel() * first.element_size()
+    sw = np.ascontiguousarray(np.asarray(src_widths if src_widths is not None else [1] * len(srcs), dtype=np.uint8))
+    dw = np.ascontiguousarray(np.asarray(dst_widths if dst_widths is not None else [1] * len(dsts), dtype=np.uint8))
+    if sw.size != len(srcs) or dw.size != len(dsts) or not np.all((sw == 1) | (sw == 2)) or \
+            not np.all((dw == 1) | (dw == 2)):
+        raise ValueError("one width of 1 or 2 per stream")
+    streams = list(zip(srcs, sw.tolist())) + list(zip(dsts, dw.tolist()))
+    first, w0 = streams[0]
+    unit = first.numel() * first.element_size() // w0
     sa, da = (ct.c_void_p * max(1, len(srcs)))(), (ct.c_void_p * max(1, len(dsts)))()
-    for arr, ts, name in ((sa, srcs, "srcs"), (da, dsts, "dsts")):
+    for arr, ts, ws, name in ((sa, srcs, sw, "srcs"), (da, dsts, dw, "dsts")):
         for i, t in enumerate(ts):
             _dev(t, f"{name}[{i}]")
-            if t.numel() * t.element_size() != nbytes:
-                raise ValueError("all probe streams must have the same byte size")
+            if t.numel() * t.element_size() != unit * int(ws[i]):
+                raise ValueError("every probe stream must hold its width times one common unit of bytes")
             arr[i] = t.data_ptr()
-    _check(lib().zero_stream_probe(sa, len(srcs), da, len(dsts), nbytes, int(order), _stream()))
+    _check(lib().zero_stream_probe(sa, _p(sw), len(srcs), da, _p(dw), len(dsts), unit, int(order), _stream()))
 
 
 # ---------------------------------------------------------------- convenience
@@ -575,23 +596,17 @@ class OwnerShard:
             self._check_bufs = (g, flag_norm[0:4].view(torch.int32), flag_norm[8:16].view(torch.float64), ws)
         return self._check_bufs
 
-    def checked_step(self, *, step: int, hyper: dict, rank_grads, grad_base: int = 0, divisor: float = 1.0,
-                     max_norm: float = 1.0, param16=None, param_base: int = 0, grid_blocks: int = 0,
-                     events=None):
-        """The two-pass step with an overflow skip and a norm clip: the rank reduce
-        with the fused check into the owner-local fp32 gradient, one 16-byte copy
-        of (overflow flag, squared norm) to the host, then -- unless the reduced
-        gradient holds a non-finite value -- AdamW from it scaled by
-        ``min(1, max_norm / (sqrt(sumsq) + 1e-6))``.
-
-        Returns ``(updated, clip_coef)``; ``updated`` is False for a skipped step
-        (nothing but the gradient buffer was written), and the caller advances
-        its step count only when it is True.  An empty owner returns (True, 1.0)
-        without a launch.  ``divisor`` folds in a static loss scale.  ``events``:
-        optional (start, end) CUDA events recorded around the reduce launch.
-        """
-        if self.end == self.begin:  # an empty owner: nothing to reduce or update
-            return True, 1.0
+    def reduce_and_check(self, *, rank_grads, grad_base: int = 0, divisor: float = 1.0, events=None):
+        """First half of the checked step: the rank reduce with the fused check into
+        the owner-local fp32 gradient, then one 16-byte copy of (overflow flag,
+        squared-norm partial) to the host.  Returns that pair for this owner;
+        an empty owner returns (0, 0.0) without a launch.  The reduce runs over
+        the owner's whole flat range, so the rank buffers hold zeros in the
+        padding between tensors (no parameter lives there).  ``divisor`` folds
+        in a static loss scale.  ``events``: optional (start, end) CUDA events
+        recorded around the reduce launch."""
+        if self.end == self.begin:
+            return 0, 0.0
         g, ov, ss, ws = self.check_buffers()
         if events is not None:
             events[0].record()
@@ -600,12 +615,42 @@ class OwnerShard:
         if events is not None:
             events[1].record()
         host = self._flag_norm.cpu().numpy()  # waits for the reduce
-        if int(host[0:4].view(np.int32)[0]):
-            return False, None
-        coef = zero_clip_coef(float(host[8:16].view(np.float64)[0]), max_norm)
+        return int(host[0:4].view(np.int32)[0]), float(host[8:16].view(np.float64)[0])
+
+    def apply_update(self, *, step: int, hyper: dict, coef: float, param16=None, param_base: int = 0,
+                     grid_blocks: int = 0) -> None:
+        """Second half: AdamW from the stored reduced gradient scaled by ``coef``
+        (nothing to do for an empty owner)."""
+        if self.end == self.begin:
+            return
+        g = self.check_buffers()[0]
         self.adam_step(step=step, hyper=hyper, reduced_g=g, param16=param16, param_base=param_base,
                        clip_coef=coef, grid_blocks=grid_blocks)
-        return True, coef
+
+    def checked_step(self, *, step: int, hyper: dict, rank_grads, grad_base: int = 0, divisor: float = 1.0,
+                     max_norm: float = 1.0, param16=None, param_base: int = 0, grid_blocks: int = 0,
+                     events=None, exchange=None):
+        """The two-pass step with an overflow skip and a global-norm clip.
+
+        ``reduce_and_check`` gives this owner's (flag, partial).  The decision
+        needs every owner's: ``exchange(flag, partial)`` returns the lists of
+        all owners' flags and partials in owner order (across GPUs, an
+        all-gather of 12 bytes per owner); without it this owner's pair stands
+        for the whole gradient.  ``zero_step_decision`` then skips when any
+        flag is set, else gives ``min(1, max_norm / (sqrt(sum of partials) +
+        1e-6))``, and ``apply_update`` runs AdamW from the stored gradient.
+
+        Returns ``(updated, clip_coef)``; every owner returns the same pair, and
+        the caller advances its step count only when ``updated`` is True.
+        """
+        flag, sumsq = self.reduce_and_check(rank_grads=rank_grads, grad_base=grad_base, divisor=divisor,
+                                            events=events)
+        flags, sums = ([flag], [sumsq]) if exchange is None else exchange(flag, sumsq)
+        updated, coef = zero_step_decision(flags, sums, max_norm)
+        if updated:
+            self.apply_update(step=step, hyper=hyper, coef=coef, param16=param16, param_base=param_base,
+                              grid_blocks=grid_blocks)
+        return updated, coef
 
     # -- export / import of fp32 shard data in the dense per-tensor layout
     def to_dense(self, owner_array, dense) -> None:

@@ -23,6 +23,11 @@ HIPCC_FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
     # no packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no mixed-precision FMAs: the compiler would otherwise fold the fp16
+    # conversion of an fma result into one v_fma_mix (one rounding of the
+    # exact a*b+c to fp16) instead of rounding the fp32 master weight that is
+    # stored, so the 16-bit copy would not always be that weight's rounding
+    "-Xclang", "-target-feature", "-Xclang", "-fma-mix-insts",
     "-Wall",
 ]
 

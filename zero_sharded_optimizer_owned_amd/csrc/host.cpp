@@ -302,6 +302,33 @@ extern "C" int zero_clip_coef(double sumsq, double max_norm, double eps, float* 
   return ZERO_OK;
 }
 
+// The step decision from every owner's check: skip when any owner saw a
+// non-finite gradient value, else clip with the norm of the whole gradient,
+// whose square is the sum of the owners' partials taken in owner order.
+extern "C" int zero_step_decision(const int32_t* overflow, const double* sumsq, uint32_t n_owners,
+                                  double max_norm, double eps, int32_t* update, float* coef) {
+  zs::clear_error();
+  if (!overflow || !sumsq || !update || !coef) return fail(ZERO_EINVAL, "zero_step_decision: NULL pointer");
+  if (n_owners == 0) return fail(ZERO_EINVAL, "zero_step_decision: no owners");
+  int32_t any = 0;
+  for (uint32_t r = 0; r < n_owners; ++r) any |= overflow[r] != 0;
+  if (any) {
+    *update = 0;
+    *coef = 0.0f;
+    return ZERO_OK;
+  }
+  double total = 0.0;
+  for (uint32_t r = 0; r < n_owners; ++r) {
+    if (!std::isfinite(sumsq[r]) || sumsq[r] < 0.0)
+      return fail(ZERO_EINVAL, "zero_step_decision: owner %u's squared norm is negative or not finite", r);
+    total += sumsq[r];
+  }
+  const int rc = zero_clip_coef(total, max_norm, eps, coef);
+  if (rc) return rc;
+  *update = 1;
+  return ZERO_OK;
+}
+
 // ---------------------------------------------------------------------------
 // ZeRO-3 per-tensor partitioning ([Deep dive] "Stage 3 needs a live working
 // set"): tensor k is cut into R shards of s_k = ceil(n_k / R) elements; rank

@@ -11,7 +11,7 @@
 //     same flat indices and only the ends of a range need scalar peels;
 //   * one block per short contiguous piece: the fused step takes one chunk
 //     of the owner's chunk table per block (or one group of short chunks),
-//     the flat-range kernels one piece of 256 (or 512) vectors, one vector
+//     the flat-range kernels one piece of 256 vectors, one vector
 //     per thread; blocks are dispatched in order, so the pieces in flight
 //     form a narrow window that advances through every stream (no
 //     cross-block synchronisation at all);
@@ -732,10 +732,18 @@ uint32_t flat_grid(uint64_t n_vec, uint64_t piece = kBlock) {
   return chunk_grid((n_vec + piece - 1) / piece, 0);
 }
 
-// Vectors per block piece of the rank reduce: one per thread, two once the
-// ranks are many (measured: 64 fp16 ranks stream faster with 8 KiB pieces of
-// each rank, one fp16 source faster with 4 KiB pieces).
-uint64_t reduce_piece(uint32_t R) { return R >= 32 ? 2 * kBlock : kBlock; }
+// Vectors per block piece of the rank reduce: one per thread.  (Two per
+// thread were 2% faster for 64 fp16 ranks dealt round-robin to the XCDs; in
+// the XCD-contiguous order with two blocks per CU that many ranks now take,
+// one per thread is 1.5-2% faster than two and 2-3% faster than four.)
+uint64_t reduce_piece(uint32_t) { return kBlock; }
+
+// The XCD-contiguous piece order (each XCD streams one contiguous run of the
+// range) for one source (measured +7.7% for a bf16 source added into fp32)
+// and from 32 sources on (+3 to +3.5% for 64 fp16 ranks with the fused check,
+// together with the two-block cap below, on two boxes); 16 sources stay
+// round-robin (the contiguous order measured -3.8% there).
+int reduce_xcd_order(uint32_t R) { return R == 1 || R >= 32 ? 1 : 0; }
 
 // Workspace of a check whose first stage has `parts` blocks: the per-block
 // (sum, flag) pairs, then the second-stage pairs.
@@ -788,10 +796,12 @@ void finish_check(const CheckOut& c, uint64_t parts, int32_t* d_overflow, double
 // Blocks of the flat reduce resident on one CU: uncapped (registers decide),
 // except two for 16 to 31 ranks of 16-bit data without the fused check
 // (measured on 16 bf16 ranks: +2.4% and +2.2% on two boxes; the same cap
-// costs one source 10% and 64 ranks 1%, and three or four blocks change
-// nothing).
+// costs one source 10%, and three or four blocks change nothing) and two
+// from 32 ranks on in the XCD-contiguous order (measured on 64 fp16 ranks
+// with the check: uncapped -2%, three per CU -1.3%; in the round-robin order
+// the cap had cost 1%).
 uint32_t reduce_lds(int dt, uint32_t R, bool check) {
-  const bool cap = dt != ZERO_F32 && R >= 16 && R < 32 && !check;
+  const bool cap = R >= 32 || (dt != ZERO_F32 && R >= 16 && !check);
   return cap ? lds_for_blocks_per_cu(2, 0) : 0;
 }
 
@@ -902,10 +912,7 @@ extern "C" int zero_reduce_owned(const void* const* rank_grads, uint32_t R, int 
   const uint64_t a0 = std::min<uint64_t>(a.end, (begin + 7) & ~7ull);
   const uint64_t a1 = std::max<uint64_t>(a0, a.end & ~7ull);
   a.piece = reduce_piece(R);
-  // One source (the microstep accumulation): XCD-contiguous runs of pieces,
-  // measured +7.7% for a bf16 source added into fp32; from 16 sources on the
-  // round-robin order is faster (-3.8% and -0.9% for 16 and 64 ranks).
-  a.xcd_order = R == 1 ? 1 : 0;
+  a.xcd_order = reduce_xcd_order(R);
   const uint32_t grid = flat_grid(a1 / 8 - a0 / 8, a.piece);
   if (check) a.chk = check_layout(workspace, grid);
   switch (grad_dtype) {
