@@ -213,6 +213,26 @@ int zero_reduce_owned(const void *const *rank_grads, uint32_t R, int grad_dtype,
                       size_t ws_bytes, hipStream_t stream);
 
 /* ----------------------------------------------------------------------------
+ * zero_reduce_owned_noalloc -- zero_reduce_owned without a workspace argument.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, results and errors as zero_reduce_owned, minus workspace and
+ * ws_bytes; it calls no allocating routine.  The check's per-block partials
+ * go to a 16 MiB array that the library keeps on every GPU it runs on until
+ * the process ends, so a check covers at most about 2.8e9 elements (larger n
+ * with a check: ERANGE, nothing launched).  Without the check outputs it is
+ * zero_reduce_owned itself.  All calls on one GPU share that array: calls
+ * that overlap on one GPU (different streams, host threads) race and must
+ * be ordered by the caller.  The first call on a device looks the array up
+ * once (EHIP if that fails).
+ * -------------------------------------------------------------------------- */
+int zero_reduce_owned_noalloc(const void *const *rank_grads, uint32_t R, int grad_dtype,
+                              uint64_t grad_base, uint64_t begin, uint64_t n, float divisor,
+                              int accumulate, float *out, uint64_t out_base, int32_t *d_overflow,
+                              double *d_sumsq, hipStream_t stream);
+
+/* ----------------------------------------------------------------------------
  * zero_check_workspace_bytes -- device workspace a check over n elements needs
  * (zero_grad_check, or zero_reduce_owned with the check outputs): the
  * per-block partial sums and flags of the first stage (one block per 2048

@@ -401,6 +401,19 @@ def test_piece_orders_are_bijections(tmp_path):
     assert run.returncode == 0 and "clean" in run.stdout, run.stdout[-2000:]
 
 
+def test_noalloc_reduce_rejects_a_check_beyond_its_scratch_before_any_device_call():
+    """zero_reduce_owned_noalloc refuses a check whose partials would not fit its
+    16 MiB scratch array (about 2.8e9 elements) with ERANGE, before touching a
+    device (this runs on the CPU)."""
+    L = zs.lib()
+    buf = (ct.c_void_p * 1)(ct.c_void_p(16))
+    flag, ss = ct.c_void_p(16), ct.c_void_p(32)
+    rc = L.zero_reduce_owned_noalloc(buf, 1, zs.ZERO_F16, 0, 0, 3_000_000_000, 1.0, 0, ct.c_void_p(64), 0,
+                                     flag, ss, None)
+    assert rc == zs.ZERO_ERANGE
+    assert "scratch" in L.zero_last_error().decode()
+
+
 def test_device_code_has_no_mixed_precision_fma():
     """The library's build flags keep the fp16 write-back a rounding of the stored
     fp32 master weight: without them the compiler folds the fp16 conversion of

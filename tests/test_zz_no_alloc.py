@@ -1,0 +1,63 @@
+"""The allocation-free checked reduce (zero_reduce_owned_noalloc) through the C ABI
+against the workspace form (zero_reduce_owned), which the other GPU tests hold
+to the oracle: two calls in a row, the second over a smaller range, each with
+identical reduced gradients, flags and squared norms (same kernels, same fold
+tree), and the gradients bit-exact against the oracle too."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import BF16, F16, assert_bits_equal, from_dev, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import zero_sharded_optimizer_owned_amd as zs  # noqa: E402
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    zs.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def test_noalloc_checked_reduce_equals_the_workspace_form_twice():
+    # the second call is smaller, so stale partials of the first would show
+    # the first call folds its partials in two stages (more than 4096 blocks)
+    cases = [(64, F16, 9_000_011, 5, 64.0 * 65536.0), (8, BF16, 100_003, 3, 8.0)]
+    for i, (R, code, n, begin, D) in enumerate(cases):
+        print(f"call {i}: R={R} dtype={code} begin={begin} n={n}", flush=True)
+        total = begin + n + 8
+        grads = [synth.host_values(synth.stream_key(40 + i, synth.STREAM_GRAD, r), 0, total, synth.DIST_NORMAL,
+                                   65.536 if code == F16 else 1e-3, code) for r in range(R)]
+        if i == 1:
+            grads[3][begin + n // 2] = 0x7F80 if code == BF16 else 0x7C00  # +inf: the flag must be set
+        dgr = [to_dev(g, code) for g in grads]
+        out_ws = torch.full((total,), 7.0, dtype=torch.float32, device=DEV)
+        out_na = torch.full((total,), 7.0, dtype=torch.float32, device=DEV)
+        ov_ws = torch.full((1,), 5, dtype=torch.int32, device=DEV)
+        ss_ws = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+        ov_na = torch.full((1,), 5, dtype=torch.int32, device=DEV)
+        ss_na = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+        ws = zs.check_workspace(n, DEV)
+        zs.zero_reduce_owned(dgr, begin, n, D, out_ws, check=(ov_ws, ss_ws, ws))
+        zs.zero_reduce_owned_noalloc(dgr, begin, n, D, out_na, check=(ov_na, ss_na))
+        torch.cuda.synchronize()
+        assert_bits_equal(from_dev(out_na), from_dev(out_ws), f"call {i} gradient")
+        assert int(ov_na.item()) == int(ov_ws.item()) == (1 if i == 1 else 0)
+        if i == 0:
+            assert ss_na.item() == ss_ws.item() and ss_ws.item() > 0
+        want = oracle.reduce([g[begin:begin + n] for g in grads], code, D)
+        assert_bits_equal(from_dev(out_na)[begin:begin + n], want, f"call {i} against the oracle")
+        assert np.all(from_dev(out_na)[:begin] == 7.0) and np.all(from_dev(out_na)[begin + n:] == 7.0)
+        # without the check it is the plain reduce
+        out_plain = torch.full((total,), 7.0, dtype=torch.float32, device=DEV)
+        zs.zero_reduce_owned_noalloc(dgr, begin, n, D, out_plain)
+        assert_bits_equal(from_dev(out_plain), from_dev(out_ws), f"call {i} unchecked")
+        del dgr, ws

@@ -31,7 +31,7 @@ EXPORTED = ("zero_last_error", "zero_shard_layout", "zero_chunk_table", "zero_de
             "zero_reduce_owned", "zero_grad_check", "zero_clip_coef", "zero_step_decision", "zero_adam_step",
             "zero_owner_to_dense", "zero_dense_to_owner", "zero3_storage", "zero3_gather_spans",
             "zero3_partition_spans", "zero_copy_spans", "zero_stream_probe",
-            "zero_check_workspace_bytes", "zero_chunk_groups", "zero_span_groups")
+            "zero_check_workspace_bytes", "zero_chunk_groups", "zero_span_groups", "zero_reduce_owned_noalloc")
 
 CHUNK_DTYPE = np.dtype([("flat", "<u8"), ("len", "<u4"), ("tensor", "<u4")])
 SPAN_DTYPE = np.dtype([("src", "<u8"), ("dst", "<u8"), ("len", "<u4"), ("buf", "<u4")])
@@ -81,6 +81,7 @@ def load(path: str):
     L.zero_dense_offsets.argtypes = [P, U32, P, P]
     L.zero_state_bytes.argtypes = [U64, U64, U32, U32, U32, P]
     L.zero_reduce_owned.argtypes = [P, U32, I, U64, U64, U64, F, I, P, U64, P, P, P, ct.c_size_t, P]
+    L.zero_reduce_owned_noalloc.argtypes = [P, U32, I, U64, U64, U64, F, I, P, U64, P, P, P]
     L.zero_grad_check.argtypes = [P, U64, P, P, P, ct.c_size_t, P]
     L.zero_clip_coef.argtypes = [D, D, D, ct.POINTER(F)]
     L.zero_step_decision.argtypes = [P, P, U32, D, D, ct.POINTER(ct.c_int32), ct.POINTER(F)]
@@ -281,6 +282,27 @@ def zero_reduce_owned(rank_grads, begin: int, n: int, divisor: float, out, *, gr
         ct.c_void_p(ov.data_ptr()) if ov is not None else None,
         ct.c_void_p(ss.data_ptr()) if ss is not None else None,
         ct.c_void_p(ws.data_ptr()) if ws is not None else None, ws_bytes, _stream()))
+
+
+def zero_reduce_owned_noalloc(rank_grads, begin: int, n: int, divisor: float, out, *, grad_base: int = 0,
+                              out_base: int = 0, accumulate: int = 0, check=None) -> None:
+    """``zero_reduce_owned`` whose check needs no workspace: ``check`` = (overflow
+    int32[1], sumsq float64[1]); the partials go to the library's own device
+    array (calls on one GPU must not overlap)."""
+    torch = _torch()
+    arr, code = _rank_ptrs(rank_grads, grad_base, begin + n)
+    _dev(out, "out", torch.float32)
+    _need(out, "out", begin + n - out_base)
+    ov = ss = None
+    if check is not None:
+        ov, ss = check
+        _dev(ov, "overflow", torch.int32)
+        _dev(ss, "sumsq", torch.float64)
+    _check(lib().zero_reduce_owned_noalloc(
+        arr, len(rank_grads), code, grad_base, begin, n, divisor, int(accumulate),
+        ct.c_void_p(out.data_ptr()), out_base,
+        ct.c_void_p(ov.data_ptr()) if ov is not None else None,
+        ct.c_void_p(ss.data_ptr()) if ss is not None else None, _stream()))
 
 
 def zero_grad_check(g, overflow, sumsq, workspace) -> None:

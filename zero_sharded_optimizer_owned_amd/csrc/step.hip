@@ -29,6 +29,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "internal.h"
 #include "launch.h"
@@ -926,6 +927,71 @@ extern "C" int zero_reduce_owned(const void* const* rank_grads, uint32_t R, int 
     if ((rc = launch_status(who))) return rc;
   }
   return ZERO_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The checked reduce without a caller workspace, for callers that cannot
+// allocate device memory.  Its per-block partials live in `scratch`, a
+// file-scope device array of kScratchBytes that every GPU the library runs on
+// holds until the process ends.  Host code never passes the array's name to a
+// kernel: the first call on a device looks up that device's address of the
+// array once, and the kernels take that address, as they take a workspace.
+// Every block of the check writes the partial it later reads, so the array
+// needs no clearing; calls that overlap on one GPU share it and race.
+// ---------------------------------------------------------------------------
+namespace zs {
+namespace {
+constexpr size_t kScratchBytes = size_t(16) << 20;  // a check over up to ~2.8e9 elements
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];  // device address of `scratch`, per device
+}  // namespace
+}  // namespace zs
+
+static __device__ __align__(256) unsigned char scratch[zs::kScratchBytes];
+
+namespace zs {
+namespace {
+int scratch_address(void** out, const char* who) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(ZERO_EHIP, "%s: no current HIP device", who);
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(ZERO_EINVAL, "%s: device %d beyond the %d this library serves", who, dev, kScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(ZERO_EHIP, "%s: looking up the scratch array on device %d failed: %s", who, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ZERO_OK;
+}
+}  // namespace
+}  // namespace zs
+
+extern "C" int zero_reduce_owned_noalloc(const void* const* rank_grads, uint32_t R, int grad_dtype,
+                                         uint64_t grad_base, uint64_t begin, uint64_t n, float divisor,
+                                         int accumulate, float* out, uint64_t out_base, int32_t* d_overflow,
+                                         double* d_sumsq, hipStream_t stream) {
+  static const char* who = "zero_reduce_owned_noalloc";
+  clear_error();
+  if (d_overflow == nullptr && d_sumsq == nullptr)  // no check: nothing needs scratch
+    return zero_reduce_owned(rank_grads, R, grad_dtype, grad_base, begin, n, divisor, accumulate, out,
+                             out_base, nullptr, nullptr, nullptr, 0, stream);
+  const uint64_t need = check_ws_bytes(check_parts(n));
+  if (need > kScratchBytes)
+    return fail(ZERO_ERANGE,
+                "%s: a check over %llu elements needs %llu bytes of partials, more than the %zu-byte "
+                "scratch array holds (use zero_reduce_owned with a workspace)",
+                who, (unsigned long long)n, (unsigned long long)need, kScratchBytes);
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws, who);
+  if (rc) return rc;
+  return zero_reduce_owned(rank_grads, R, grad_dtype, grad_base, begin, n, divisor, accumulate, out, out_base,
+                           d_overflow, d_sumsq, ws, kScratchBytes, stream);
 }
 
 extern "C" int zero_check_workspace_bytes(uint64_t n, uint64_t* bytes) {
