@@ -112,7 +112,15 @@ PROBE_STRUCTURE = {
     "reduce_add_mean_bf16_r16": ([1] * 16 + [2], [2]),            # 16 ranks and acc in; acc out
     "owner_to_dense": ([2], [2]),
     "span_kernel<uint16_t>": ([1], [1]),
+    # second kernels of a step
+    "adam_step_reduced_f16": ([2] * 4, [2] * 3 + [1]),            # g, w, m, v in; w m v p16 out
+    "adam_step_reduced_bf16": ([2] * 4, [2] * 3 + [1]),
+    "adam_step_f32_bf16_r16": ([2] * 19, [2] * 3 + [1]),          # 16 fp32 ranks, w m v in
 }
+
+# The second kernel of a step (after the dominant one), timed beside it.
+SECOND_KERNEL = {(4, "accumulate"): "adam_step_reduced_f16", (5, "accumulate"): "adam_step_f32_bf16_r16",
+                 (5, "per-backward"): "adam_step_reduced_bf16"}
 
 
 def structure_name(kname: str) -> str:
@@ -193,16 +201,21 @@ def step_stats(ms: list) -> dict | None:
             "mean": round(sum(v) / len(v), 4)}
 
 
-def ceilings(kname: str, elements: int) -> dict:
+def ceilings(kname: str, elements: int, second=None) -> dict:
     """Measured ceilings for the dominant kernel: one stream read, one written,
     a plain copy, the probe with the kernel's own read:write byte mix over
     equal streams, and the probe with the kernel's exact stream structure and
-    size (``elements`` per stream)."""
+    size (``elements`` per stream).  ``second``: (kernel, elements) of the
+    step's second kernel, whose exact-structure probe is measured too."""
     n_src, n_dst = PROBE_MIX[kname]
-    return {"read_gbps": round(probe_gbps(1, 0), 1), "write_gbps": round(probe_gbps(0, 1), 1),
-            "copy_gbps": round(probe_gbps(1, 1), 1), "mix": f"{n_src}:{n_dst}",
-            "mix_gbps": round(probe_gbps(n_src, n_dst), 1), "structure": structure_name(kname),
-            "structure_gbps": round(probe_structure_gbps(kname, elements), 1), "kernel": "zero_stream_probe"}
+    out = {"read_gbps": round(probe_gbps(1, 0), 1), "write_gbps": round(probe_gbps(0, 1), 1),
+           "copy_gbps": round(probe_gbps(1, 1), 1), "mix": f"{n_src}:{n_dst}",
+           "mix_gbps": round(probe_gbps(n_src, n_dst), 1), "structure": structure_name(kname),
+           "structure_gbps": round(probe_structure_gbps(kname, elements), 1), "kernel": "zero_stream_probe"}
+    if second is not None:
+        out["second_structure"] = structure_name(second[0])
+        out["second_structure_gbps"] = round(probe_structure_gbps(*second), 1)
+    return out
 
 
 def with_ceiling(roofline: dict, ceil: dict) -> dict:
@@ -211,8 +224,9 @@ def with_ceiling(roofline: dict, ceil: dict) -> dict:
                 frac_of_structure=round(a / ceil["structure_gbps"], 4))
 
 
-def dominant_elements(args) -> int:
-    """Elements the dominant kernel of a run processes per launch, from the layout
+def dominant_elements(args, owned: bool = False) -> int:
+    """Elements the dominant kernel of a run processes per launch (``owned``: the
+    owner's real elements, which the second kernel updates), from the layout
     alone (the ceilings are measured before the workload takes its memory)."""
     import zero_sharded_optimizer_owned_amd as zs
 
@@ -225,10 +239,10 @@ def dominant_elements(args) -> int:
         numels, R = {2: ([1_500_000_000], 4), 3: (llama_numels(), 8), 4: ([70_000_000_000], 64),
                      5: (config5_numels(), 16)}[args.config]
     off, total, b, e = zs.zero_shard_layout(numels, R, 64)
-    if args.config == 5 and args.schedule == "accumulate" and args.op == "step":
+    if args.config == 5 and args.schedule == "accumulate" and args.op == "step" and not owned:
         return total
     begin, end = int(b[1]), int(e[1])
-    if (args.config == 4 or args.schedule == "per-backward") and args.op == "step":
+    if (args.config == 4 or args.schedule == "per-backward") and args.op == "step" and not owned:
         return end - begin
     return sum(max(0, min(end, int(o) + n) - max(begin, int(o))) for o, n in zip(off, numels))
 
@@ -405,6 +419,15 @@ class Workload:
         gw = self.grads[0].element_size() if self.grads[0] is not None else 4
         return n * (self.R * gw + 24 + self.p16.element_size())
 
+    def second_bytes(self) -> int:
+        """Algorithmic bytes of the step's second kernel: AdamW from a stored fp32
+        gradient (configs 4 and 5 per-backward: 4 + 12 read, 12 + 2 written) or
+        config 5's fused owner step (16 fp32 ranks + 12 read, 14 written)."""
+        n = self.sh.n_real
+        if self.cfg == 5 and self.schedule == "accumulate":
+            return n * (self.R * 4 + 26)
+        return n * 30
+
     def step_bytes(self, overflow: bool) -> int:
         n = self.sh.n_real
         if self.cfg == 4:
@@ -417,8 +440,9 @@ class Workload:
             return P * (6 + 7 * 10) + n * (self.R * 4 + 26)
         return self.kernel_bytes
 
-    # one full step of the owner's hot path
-    def step(self, timing=None):
+    # one full step of the owner's hot path; ``timing``: events around the dominant
+    # kernel, ``timing2``: around the second kernel (configs 4 and 5)
+    def step(self, timing=None, timing2=None):
         import torch
 
         import zero_sharded_optimizer_owned_amd as zs
@@ -433,8 +457,12 @@ class Workload:
                                      accumulate=0 if k == 0 else 2)
                 if timing is not None and k == 7:
                     timing[1].record()
+            if timing2 is not None:
+                timing2[0].record()
             sh.adam_step(step=self.t, hyper=HP, reduced_g=self.acc_owned, param16=self.p16,
                          param_base=self.param_base, grid_blocks=self.grid)
+            if timing2 is not None:
+                timing2[1].record()
             self.t += 1
             return False
         if self.cfg == 5:
@@ -444,9 +472,13 @@ class Workload:
                 zs.zero_reduce_owned([g], 0, sh.padded_total, 1.0, self.acc, accumulate=k > 0)
                 if timing is not None and k == 7:
                     timing[1].record()
+            if timing2 is not None:
+                timing2[0].record()
             sh.adam_step(step=self.t, hyper=HP, rank_grads=self.grads, grad_base=sh.local_base,
                          divisor=self.divisor, param16=self.p16, param_base=self.param_base,
                          grid_blocks=self.grid)
+            if timing2 is not None:
+                timing2[1].record()
             self.t += 1
             return False
         self.calls += 1
@@ -459,7 +491,8 @@ class Workload:
             # reduce + check, 16 bytes to the host, then AdamW from g unless overflowed
             updated, _ = sh.checked_step(step=self.t, hyper=HP, rank_grads=self.grads, grad_base=sh.local_base,
                                          divisor=self.divisor, max_norm=self.max_norm, param16=self.p16,
-                                         param_base=self.param_base, grid_blocks=self.grid, events=timing)
+                                         param_base=self.param_base, grid_blocks=self.grid, events=timing,
+                                         apply_events=timing2)
             if inject:
                 self.grads[5][12345] = saved[0]
                 self.grads[17][777_777] = saved[1]
@@ -713,6 +746,21 @@ def gather3_bench(args, ceil):
     print(json.dumps(line), flush=True)
 
 
+def whole_line_bytes(ranges, streams, line: int = 128, sector: int = 32) -> int:
+    """Bytes that the owner's real ranges take in whole memory units: a read
+    stream fetches every 128-byte line that holds one of its elements, a write
+    stream writes every 32-byte sector that holds one.  ``streams``: (element
+    bytes, index of the stream's first element (its base is 256-byte aligned),
+    True for a read)."""
+    total = 0
+    for b, e in ranges:
+        for size, base, read in streams:
+            unit = line if read else sector
+            lo, hi = (b - base) * size, (e - base) * size
+            total += (-(-hi // unit) - lo // unit) * unit
+    return total
+
+
 def small_bench(args, ceil):
     """The fused fp16 step (R=4, AdamW, fp16 write-back) of owner 1 over
     2,000,000 tensors of 100 elements each, padded to 128 (1.7 GB per step, far
@@ -760,6 +808,11 @@ def small_bench(args, ceil):
     ms = timed(True)
     n = sh.n_real
     nbytes = n * (R * 2 + 26)
+    # what whole lines (reads) and sectors (writes) of the padded slots come to:
+    # 4 fp16 rank slices and master/m/v read, master/m/v and the fp16 copy written
+    ranges = [(int(c["flat"]), int(c["flat"]) + int(c["len"])) for c in sh.chunks]
+    streams = [(2, lb, True)] * R + [(4, lb, True)] * 3 + [(4, lb, False)] * 3 + [(2, 0, False)]
+    line_bytes = whole_line_bytes(ranges, streams)
     achieved = nbytes / (ms / 1e3) / 1e9
     line = {
         "metric": "owned-shard params updated/sec + achieved HBM GB/s (fraction of MI355X peak)",
@@ -777,6 +830,8 @@ def small_bench(args, ceil):
                      "bytes_per_element": float(R * 2 + 26)},
         "one_block_per_chunk": {"ms": round(ms_chunk, 4),
                                 "achieved_gbps": round(nbytes / (ms_chunk / 1e3) / 1e9, 1)},
+        "whole_line_bytes_per_launch": line_bytes,
+        "whole_line_gbps": round(line_bytes / (ms / 1e3) / 1e9, 1),
     }
     if ceil:
         line["ceiling"] = with_ceiling(line["roofline"], ceil)
@@ -865,7 +920,9 @@ def main():
         kname = {2: "adam_step_f16_f16", 3: "adam_step_bf16_bf16", 4: "reduce_check_f16_r64",
                  5: "accumulate_bf16"}[args.config]
     # before the workload takes its memory
-    ceil = None if args.no_ceiling else ceilings(kname, dominant_elements(args))
+    kname2 = SECOND_KERNEL.get((args.config, args.schedule)) if args.op == "step" else None
+    second = (kname2, dominant_elements(args, owned=True)) if kname2 else None
+    ceil = None if args.no_ceiling else ceilings(kname, dominant_elements(args), second)
     if args.calibrate_copy:
         # a plain copy of known size: 2^28 fp32 read + 2^28 fp32 written per launch
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -886,6 +943,8 @@ def main():
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    starts2 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends2 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     overflow_steps = 0
     w.skipped = 0
     torch.cuda.synchronize()
@@ -894,7 +953,7 @@ def main():
     marks[0].record()
     launched = []
     for i in range(args.steps):
-        skipped = w.step(timing=(starts[i], ends[i]))
+        skipped = w.step(timing=(starts[i], ends[i]), timing2=(starts2[i], ends2[i]))
         marks[i + 1].record()
         launched.append(not skipped)
         overflow_steps += int(skipped)
@@ -932,6 +991,18 @@ def main():
     }
     if ceil:
         line["ceiling"] = with_ceiling(roofline, ceil)
+    k2 = [s2.elapsed_time(e2) for s2, e2, ok in zip(starts2, ends2, launched) if ok] if kname2 else []
+    if k2:  # the step's second kernel, on the steps that run it (config 4: updating steps)
+        ms2 = sum(k2) / len(k2)
+        bytes2 = w.second_bytes()
+        sk = {"kernel": kname2, "kernel_ms": round(ms2, 4), "bytes_per_launch": bytes2,
+              "achieved": round(bytes2 / (ms2 / 1e3) / 1e9, 1),
+              "frac": round(bytes2 / (ms2 / 1e3) / 1e9 / PEAK_GBPS, 4)}
+        if ceil:
+            sk["structure"] = ceil["second_structure"]
+            sk["structure_gbps"] = ceil["second_structure_gbps"]
+            sk["frac_of_structure"] = round(sk["achieved"] / ceil["second_structure_gbps"], 4)
+        line["second_kernel"] = sk
     if args.config == 4:  # updating and skipped (overflow) steps separately, and the 4-step cycle
         line["step_ms_update"] = step_stats([t for t, ok in zip(step_ms, launched) if ok])
         line["step_ms_overflow"] = step_stats([t for t, ok in zip(step_ms, launched) if not ok])

@@ -61,3 +61,17 @@ def test_every_timed_kernel_has_a_probe_mix():
                   "reduce_add_mean_bf16_r16", "owner_to_dense", "span_kernel<uint16_t>"):
         reads, writes = bench.PROBE_MIX[kname]
         assert reads > 0 and writes > 0
+
+
+def test_every_timed_kernel_has_an_exact_structure():
+    """The exact-structure probe of each timed kernel: its stream widths add up to
+    its algorithmic bytes per element (2 bytes per width unit)."""
+    per_element = {"adam_step_f16_f16": 34, "adam_step_bf16_bf16": 42, "reduce_check_f16_r64": 132,
+                   "accumulate_bf16": 10, "reduce_add_mean_bf16_r16": 40, "owner_to_dense": 8,
+                   "span_kernel<uint16_t>": 4, "adam_step_reduced_f16": 30, "adam_step_reduced_bf16": 30,
+                   "adam_step_f32_bf16_r16": 90}
+    for kname, b in per_element.items():
+        src, dst = bench.PROBE_STRUCTURE[kname]
+        assert 2 * (sum(src) + sum(dst)) == b, kname
+    for kname in bench.SECOND_KERNEL.values():
+        assert kname in bench.PROBE_STRUCTURE

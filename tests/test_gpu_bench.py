@@ -59,6 +59,10 @@ def test_default_bench_line_keeps_the_contract():
     assert 0.3 < r["frac"] < 1.0
     # counter-measured bytes, or null once the kernel source has changed since the counters
     assert r["traffic"] is None or r["traffic"] >= r["bytes_per_launch"]
+    if d["steps"] > d["overflow_steps"]:  # AdamW from the stored gradient, on the updating steps
+        k2 = d["second_kernel"]
+        assert k2["kernel"] == "adam_step_reduced_f16" and k2["bytes_per_launch"] == 1_093_750_000 * 30
+        assert k2["achieved"] == pytest.approx(k2["bytes_per_launch"] / (k2["kernel_ms"] * 1e-3) / 1e9, rel=1e-3)
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["unit"] == "params/s" and c["value"] > 0 and c["cores"] >= 1
     assert c["sample"] and c["bytes_per_param"] == 162.0

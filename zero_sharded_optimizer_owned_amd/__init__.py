@@ -651,7 +651,7 @@ class OwnerShard:
 
     def checked_step(self, *, step: int, hyper: dict, rank_grads, grad_base: int = 0, divisor: float = 1.0,
                      max_norm: float = 1.0, param16=None, param_base: int = 0, grid_blocks: int = 0,
-                     events=None, exchange=None):
+                     events=None, exchange=None, apply_events=None):
         """The two-pass step with an overflow skip and a global-norm clip.
 
         ``reduce_and_check`` gives this owner's (flag, partial).  The decision
@@ -664,14 +664,20 @@ class OwnerShard:
 
         Returns ``(updated, clip_coef)``; every owner returns the same pair, and
         the caller advances its step count only when ``updated`` is True.
+        ``events`` / ``apply_events``: optional (start, end) CUDA events
+        recorded around the reduce and around the AdamW launch.
         """
         flag, sumsq = self.reduce_and_check(rank_grads=rank_grads, grad_base=grad_base, divisor=divisor,
                                             events=events)
         flags, sums = ([flag], [sumsq]) if exchange is None else exchange(flag, sumsq)
         updated, coef = zero_step_decision(flags, sums, max_norm)
         if updated:
+            if apply_events is not None:
+                apply_events[0].record()
             self.apply_update(step=step, hyper=hyper, coef=coef, param16=param16, param_base=param_base,
                               grid_blocks=grid_blocks)
+            if apply_events is not None:
+                apply_events[1].record()
         return updated, coef
 
     # -- export / import of fp32 shard data in the dense per-tensor layout

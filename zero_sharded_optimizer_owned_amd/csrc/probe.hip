@@ -13,8 +13,7 @@ namespace {
 struct ProbeArgs {
   const uint4* src[ZERO_MAX_PROBE_STREAMS];
   uint4* dst[ZERO_MAX_PROBE_STREAMS];
-  uint8_t src_w[ZERO_MAX_PROBE_STREAMS];  // 16-byte vectors per thread: 1 or 2
-  uint8_t dst_w[ZERO_MAX_PROBE_STREAMS];
+  uint64_t src_wide, dst_wide;  // bit s set: stream s takes 2 vectors per thread, else 1
   uint32_t n_src, n_dst;
   uint64_t n_vec;  // threads' worth of work: a stream of width w holds w * n_vec vectors
   int xcd_order;   // pieces in XCD-contiguous runs (xcd_contiguous)
@@ -40,26 +39,37 @@ __global__ void __launch_bounds__(kBlock) probe_kernel(const ProbeArgs a) {
     uint4 x = zero;
     for (uint32_t s0 = 0; s0 < a.n_src; s0 += kProbeBatch) {
       const uint32_t nb = min((uint32_t)kProbeBatch, a.n_src - s0);
-      uint4 y[kProbeBatch][2];
+      uint4 y[kProbeBatch], z[kProbeBatch];
 #pragma unroll
       for (int j = 0; j < kProbeBatch; ++j) {
-        const uint32_t w = j < (int)nb ? a.src_w[s0 + j] : 0;
-        y[j][0] = w ? a.src[s0 + j][w * i] : zero;
-        y[j][1] = w == 2 ? a.src[s0 + j][w * i + 1] : zero;
+        y[j] = zero;
+        z[j] = zero;
+        if (j < (int)nb) {
+          const uint4* p = a.src[s0 + j];
+          if ((a.src_wide >> (s0 + j)) & 1) {
+            y[j] = p[2 * i];
+            z[j] = p[2 * i + 1];
+          } else {
+            y[j] = p[i];
+          }
+        }
       }
 #pragma unroll
       for (int j = 0; j < kProbeBatch; ++j) {
-        x.x ^= y[j][0].x ^ y[j][1].x;
-        x.y ^= y[j][0].y ^ y[j][1].y;
-        x.z ^= y[j][0].z ^ y[j][1].z;
-        x.w ^= y[j][0].w ^ y[j][1].w;
+        x.x ^= y[j].x ^ z[j].x;
+        x.y ^= y[j].y ^ z[j].y;
+        x.z ^= y[j].z ^ z[j].z;
+        x.w ^= y[j].w ^ z[j].w;
       }
     }
     asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
     for (uint32_t d = 0; d < a.n_dst; ++d) {
-      const uint32_t w = a.dst_w[d];
-      a.dst[d][w * i] = x;
-      if (w == 2) a.dst[d][w * i + 1] = x;
+      if ((a.dst_wide >> d) & 1) {
+        a.dst[d][2 * i] = x;
+        a.dst[d][2 * i + 1] = x;
+      } else {
+        a.dst[d][i] = x;
+      }
     }
   }
 }
@@ -86,16 +96,17 @@ extern "C" int zero_stream_probe(const void* const* srcs, const uint8_t* src_wid
     if (!srcs[s] || !aligned16(srcs[s]))
       return fail(ZERO_EINVAL, "%s: source %u is NULL or not 16-byte aligned", who, s);
     a.src[s] = static_cast<const uint4*>(srcs[s]);
-    a.src_w[s] = src_widths ? src_widths[s] : 1;
-    if (a.src_w[s] != 1 && a.src_w[s] != 2) return fail(ZERO_EINVAL, "%s: source %u has width %u", who, s, a.src_w[s]);
+    const unsigned w = src_widths ? src_widths[s] : 1;
+    if (w != 1 && w != 2) return fail(ZERO_EINVAL, "%s: source %u has width %u", who, s, w);
+    if (w == 2) a.src_wide |= 1ull << s;
   }
   for (uint32_t d = 0; d < n_dst; ++d) {
     if (!dsts[d] || !aligned16(dsts[d]))
       return fail(ZERO_EINVAL, "%s: destination %u is NULL or not 16-byte aligned", who, d);
     a.dst[d] = static_cast<uint4*>(dsts[d]);
-    a.dst_w[d] = dst_widths ? dst_widths[d] : 1;
-    if (a.dst_w[d] != 1 && a.dst_w[d] != 2)
-      return fail(ZERO_EINVAL, "%s: destination %u has width %u", who, d, a.dst_w[d]);
+    const unsigned w = dst_widths ? dst_widths[d] : 1;
+    if (w != 1 && w != 2) return fail(ZERO_EINVAL, "%s: destination %u has width %u", who, d, w);
+    if (w == 2) a.dst_wide |= 1ull << d;
   }
   if (bytes == 0) return ZERO_OK;
   a.n_src = n_src;
