@@ -1,6 +1,7 @@
 // Sanitizer driver for the host half of libzero_shard (test infrastructure):
 // layouts, chunk tables (counted, then filled, then with too small a
-// capacity), state accounting, the clip scalar and the stage-3 span builders
+// capacity), dense offsets, state accounting, the clip scalar, the step
+// decision over all owners and the stage-3 span builders
 // over random tensor lists, plus the argument errors, in an
 // AddressSanitizer / UndefinedBehaviorSanitizer build.  It also checks the
 // chunk table's coverage: every real element of an owner exactly once, no
@@ -83,6 +84,19 @@ int main() {
     expect(zero_state_bytes(1 + below(1ull << 40), R, 2, 2, 12, q) == ZERO_OK, "state bytes", trial);
     float coef = 0.0f;
     expect(zero_clip_coef((double)below(1000), 1.0, 1e-6, &coef) == ZERO_OK, "clip", trial);
+    std::vector<int32_t> flags(R);
+    std::vector<double> partial(R);
+    for (uint32_t r = 0; r < R; ++r) {
+      flags[r] = below(50) == 0;
+      partial[r] = (double)below(1000);
+    }
+    int32_t update = -1;
+    expect(zero_step_decision(flags.data(), partial.data(), R, 1.0, 1e-6, &update, &coef) == ZERO_OK,
+           "step decision", trial);
+    std::vector<uint64_t> doff(T);
+    uint64_t dtotal = 0;
+    expect(zero_dense_offsets(numel.data(), T, doff.data(), &dtotal) == ZERO_OK && dtotal >= T,
+           "dense offsets", trial);
 
     std::vector<uint32_t> live;
     for (uint32_t k = 0; k < T; ++k)

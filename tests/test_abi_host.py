@@ -431,3 +431,31 @@ def test_device_code_has_no_mixed_precision_fma():
     asm = res.stdout
     assert "v_fma_mix" not in asm and "v_mad_mix" not in asm
     assert "v_cvt_f16_f32" in asm
+
+
+def test_step_decision_is_the_unsharded_clip_and_skip():
+    """zero_step_decision: any owner's flag skips the step; otherwise the clip factor
+    is the oracle's clip of the owners' partial norms summed in owner order (the
+    whole gradient's squared norm), rounded once to fp32."""
+    rnd = random.Random(9)
+    for _ in range(300):
+        n = rnd.randrange(1, 70)
+        parts = [rnd.choice([0.0, rnd.random() * 10 ** rnd.randrange(-8, 4)]) for _ in range(n)]
+        max_norm = rnd.choice([1.0, 0.5, 8.0, 1e-3])
+        updated, coef = zs.zero_step_decision([0] * n, parts, max_norm)
+        total = 0.0
+        for p in parts:  # owner order
+            total += p
+        assert updated and coef == np.float32(oracle.clip_coef(total, max_norm))
+        flags = [0] * n
+        flags[rnd.randrange(n)] = rnd.choice([1, 7, -1])
+        assert zs.zero_step_decision(flags, parts, max_norm) == (False, None)
+    # a skipped step does not look at the partials (they are meaningless after an overflow)
+    assert zs.zero_step_decision([0, 1], [float("nan"), 1.0]) == (False, None)
+    for bad in (([0], [float("nan")]), ([0], [-1.0]), ([0], [float("inf")])):
+        with pytest.raises(zs.ZeroShardError):
+            zs.zero_step_decision(*bad)
+    with pytest.raises(zs.ZeroShardError):
+        zs.zero_step_decision([], [])
+    with pytest.raises(zs.ZeroShardError):
+        zs.zero_step_decision([0], [1.0], max_norm=0.0)
