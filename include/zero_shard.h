@@ -225,7 +225,7 @@ int zero_reduce_owned(const void *const *rank_grads, uint32_t R, int grad_dtype,
  * zero_reduce_owned itself.  All calls on one GPU share that array: calls
  * that overlap on one GPU (different streams, host threads) race and must
  * be ordered by the caller.  The first call on a device looks the array up
- * once (EHIP if that fails).
+ * once (EHIP if that fails); make that first call outside graph capture.
  * -------------------------------------------------------------------------- */
 int zero_reduce_owned_noalloc(const void *const *rank_grads, uint32_t R, int grad_dtype,
                               uint64_t grad_base, uint64_t begin, uint64_t n, float divisor,

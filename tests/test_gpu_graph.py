@@ -97,3 +97,42 @@ def test_checked_reduce_in_a_graph_replays_like_eager():
         assert np.array_equal(_bits(out[begin:]), want[0]), f"replay {replay}: reduced gradient differs"
         assert torch.all(out[:begin] == -1.0), f"replay {replay}: wrote below begin"
         assert (int(ov.item()), float(ss.item())) == want[1:], f"replay {replay}: flag or norm differs"
+
+
+def test_allocation_free_checked_reduce_in_a_graph_replays_like_eager():
+    """The allocation-free checked reduce, for callers under graph capture: captured
+    after a first eager call on the device (which looks up its scratch array) and
+    replayed three times with eager work, and a workspace-form reduce over other
+    data, between the replays; every replay gives the eager result."""
+    R, begin, n = 5, 3, 9_000_011
+    grads = [to_dev(gen(8, synth.STREAM_GRAD, begin + n, synth.DIST_NORMAL, 65.536, F16, rank=r), F16)
+             for r in range(R)]
+    out = torch.empty(begin + n, dtype=torch.float32, device=DEV)
+    ov = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ss = torch.zeros(1, dtype=torch.float64, device=DEV)
+
+    def reduce():
+        zs.zero_reduce_owned_noalloc(grads, begin, n, float(R) * 65536, out, check=(ov, ss))
+
+    reduce()
+    torch.cuda.synchronize()
+    want = (_bits(out[begin:]), int(ov.item()), float(ss.item()))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        reduce()
+    other = torch.ones(1 << 20, dtype=torch.float16, device=DEV)
+    o_out = torch.empty(1 << 20, dtype=torch.float32, device=DEV)
+    o_ov = torch.zeros(1, dtype=torch.int32, device=DEV)
+    o_ss = torch.zeros(1, dtype=torch.float64, device=DEV)
+    for replay in range(3):
+        out.fill_(-1.0)
+        ov.fill_(7)
+        ss.fill_(-1.0)
+        torch.randn(4096, device=DEV).sum()
+        # an eager allocation-free call on other data in between: it shares the scratch array
+        zs.zero_reduce_owned_noalloc([other], 0, other.numel(), 1.0, o_out, check=(o_ov, o_ss))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert float(o_ss.item()) == other.numel() and int(o_ov.item()) == 0
+        assert np.array_equal(_bits(out[begin:]), want[0]), f"replay {replay}: reduced gradient differs"
+        assert (int(ov.item()), float(ss.item())) == want[1:], f"replay {replay}: flag or norm differs"
