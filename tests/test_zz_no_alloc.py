@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import BF16, F16, assert_bits_equal, from_dev, to_dev
+from helpers import BF16, F16, F32, assert_bits_equal, from_dev, to_dev
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -60,4 +60,36 @@ def test_noalloc_checked_reduce_equals_the_workspace_form_twice():
         out_plain = torch.full((total,), 7.0, dtype=torch.float32, device=DEV)
         zs.zero_reduce_owned_noalloc(dgr, begin, n, D, out_plain)
         assert_bits_equal(from_dev(out_plain), from_dev(out_ws), f"call {i} unchecked")
+        del dgr, ws
+
+
+def test_noalloc_accumulate_modes_equal_the_workspace_form():
+    # accumulate 1 (out = (out + sum) / D) and 2 (out = out + sum / D) start from the
+    # same fp32 contents on both sides; the second call is again the smaller one
+    R, code, D = 16, BF16, 16.0
+    for i, (mode, n, begin) in enumerate([(1, 600_001, 3), (2, 70_007, 11)]):
+        print(f"accumulate {mode}: R={R} begin={begin} n={n}", flush=True)
+        total = begin + n + 8
+        grads = [synth.host_values(synth.stream_key(50 + i, synth.STREAM_GRAD, r), 0, total, synth.DIST_NORMAL,
+                                   1e-3, code) for r in range(R)]
+        start = synth.host_values(synth.stream_key(50 + i, synth.STREAM_MASTER, 0), 0, total, synth.DIST_NORMAL,
+                                  1e-2, F32)
+        dgr = [to_dev(g, code) for g in grads]
+        out_ws, out_na = to_dev(start, F32), to_dev(start, F32)
+        ov_ws = torch.full((1,), 5, dtype=torch.int32, device=DEV)
+        ss_ws = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+        ov_na = torch.full((1,), 5, dtype=torch.int32, device=DEV)
+        ss_na = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+        ws = zs.check_workspace(n, DEV)
+        zs.zero_reduce_owned(dgr, begin, n, D, out_ws, accumulate=mode, check=(ov_ws, ss_ws, ws))
+        zs.zero_reduce_owned_noalloc(dgr, begin, n, D, out_na, accumulate=mode, check=(ov_na, ss_na))
+        torch.cuda.synchronize()
+        assert_bits_equal(from_dev(out_na), from_dev(out_ws), f"accumulate {mode}")
+        assert int(ov_na.item()) == int(ov_ws.item()) == 0
+        assert ss_na.item() == ss_ws.item() and ss_ws.item() > 0
+        part = [g[begin:begin + n] for g in grads]
+        acc = start.view(np.float32)[begin:begin + n].copy()
+        want = oracle.reduce(part, code, D, out=acc, accumulate=True) if mode == 1 else \
+            oracle.reduce_add(part, code, D, acc)
+        assert_bits_equal(from_dev(out_na)[begin:begin + n], want, f"accumulate {mode} against the oracle")
         del dgr, ws
