@@ -26,7 +26,9 @@
  *     No exceptions escape, nothing exits the process.
  *   - The caller owns every buffer.  The library allocates no memory and
  *     keeps no state between calls apart from a read-only cache of each
- *     device's LDS sizes.  Arguments are validated before anything is
+ *     device's LDS sizes, and, for zero_reduce_owned_noalloc only, its
+ *     static device scratch array and that array's address on each device
+ *     (see there).  Arguments are validated before anything is
  *     launched; a call that fails validation launches nothing and writes
  *     nothing.  Buffer extents cannot be seen through plain pointers: the
  *     caller guarantees the sizes stated for each argument.
