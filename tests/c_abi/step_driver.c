@@ -16,11 +16,16 @@
  * Outputs: master, m, v after the fused step; the 16-bit copy
  *   (padded_total values, zero before the step); the reduced gradient of a
  *   separate checked reduce (end - local_base fp32, zero outside the owner
- *   range); its overflow flag (i32) and squared norm (f64).
+ *   range); its overflow flag (i32) and squared norm (f64); the step decision
+ *   for this owner alone with max_norm 1 and eps 1e-6 (update i32, clip
+ *   factor f32); the dense layout (dense_total u64, then dense_offset u64
+ *   [n_tensors]).
  *
- * The program also checks the error convention: a call with step 0 must
- * return ZERO_EINVAL with a message.  Exit status 0 on success, 1 on any
- * failure (with a message on stderr).
+ * The program also checks, on its own: the error convention (a call with
+ * step 0 must return ZERO_EINVAL with a message); that the allocation-free
+ * checked reduce gives the same bits, flag and norm as the workspace form;
+ * and that the decision's factor equals zero_clip_coef of the same norm.
+ * Exit status 0 on success, 1 on any failure (with a message on stderr).
  */
 #include <stdint.h>
 #include <stdio.h>
@@ -97,7 +102,7 @@ int main(int argc, char** argv) {
 
   /* inputs to the device */
   const size_t gsz = gdt == ZERO_F32 ? 4 : 2, nloc = (size_t)(end - lb);
-  void* h_grad = malloc(total * gsz ? total * gsz : 1);
+  void* h_grad = malloc(total * gsz > 0 ? total * gsz : 1);
   const void** d_grads = malloc(R * sizeof *d_grads);
   for (uint64_t r = 0; r < R; ++r) {
     read_all(in, h_grad, total * gsz, "rank gradients");
@@ -161,6 +166,16 @@ int main(int argc, char** argv) {
   ZS(zero_adam_step(&a, stream));
   ZS(zero_reduce_owned((const void* const*)d_grads, (uint32_t)R, gdt, 0, begin, end - begin, (float)R, 0,
                        d_g, lb, d_flag, d_sumsq, d_ws, (size_t)ws_bytes, stream));
+  /* the same checked reduce without a workspace: identical bits, flag and norm */
+  float* d_g2 = NULL;
+  int32_t* d_flag2 = NULL;
+  double* d_sumsq2 = NULL;
+  HIP(hipMalloc((void**)&d_g2, nloc * 4 + 16));
+  HIP(hipMemset(d_g2, 0, nloc * 4 + 16));
+  HIP(hipMalloc((void**)&d_flag2, sizeof(int32_t)));
+  HIP(hipMalloc((void**)&d_sumsq2, sizeof(double)));
+  ZS(zero_reduce_owned_noalloc((const void* const*)d_grads, (uint32_t)R, gdt, 0, begin, end - begin, (float)R, 0,
+                               d_g2, lb, d_flag2, d_sumsq2, stream));
   HIP(hipStreamSynchronize(stream));
 
   FILE* out = fopen(argv[2], "wb");
@@ -182,6 +197,32 @@ int main(int argc, char** argv) {
   HIP(hipMemcpy(&sumsq, d_sumsq, sizeof sumsq, hipMemcpyDeviceToHost));
   write_all(out, &flag, sizeof flag);
   write_all(out, &sumsq, sizeof sumsq);
+
+  float* h_f2 = malloc(nloc * 4 + 1);
+  int32_t flag2 = -1;
+  double sumsq2 = -1.0;
+  HIP(hipMemcpy(h_f2, d_g2, nloc * 4, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(&flag2, d_flag2, sizeof flag2, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(&sumsq2, d_sumsq2, sizeof sumsq2, hipMemcpyDeviceToHost));
+  if (memcmp(h_f, h_f2, nloc * 4) != 0) FAIL("the allocation-free reduce differs from the workspace form");
+  if (flag2 != flag || memcmp(&sumsq2, &sumsq, sizeof sumsq) != 0)
+    FAIL("the allocation-free check differs: flag %d/%d, sumsq %.17g/%.17g", flag2, flag, sumsq2, sumsq);
+
+  int32_t update = -1;
+  float coef = -1.0f, coef1 = -2.0f;
+  ZS(zero_step_decision(&flag, &sumsq, 1, 1.0, 1e-6, &update, &coef));
+  if (!flag) {
+    ZS(zero_clip_coef(sumsq, 1.0, 1e-6, &coef1));
+    if (update != 1 || coef != coef1) FAIL("decision (%d, %.9g) against zero_clip_coef %.9g", update, coef, coef1);
+  }
+  write_all(out, &update, sizeof update);
+  write_all(out, &coef, sizeof coef);
+
+  uint64_t* dense = malloc(n_tensors * sizeof *dense);
+  uint64_t dense_total = 0;
+  ZS(zero_dense_offsets(numel, (uint32_t)n_tensors, dense, &dense_total));
+  write_all(out, &dense_total, sizeof dense_total);
+  write_all(out, dense, n_tensors * sizeof *dense);
   if (fclose(out) != 0) FAIL("cannot write %s", argv[2]);
 
   HIP(hipStreamDestroy(stream));
@@ -195,8 +236,11 @@ int main(int argc, char** argv) {
   HIP(hipFree(d_ws));
   HIP(hipFree(d_flag));
   HIP(hipFree(d_sumsq));
+  HIP(hipFree(d_g2));
+  HIP(hipFree(d_flag2));
+  HIP(hipFree(d_sumsq2));
   free(numel), free(offs), free(obeg), free(oend), free(chunks), free(h_grad), free(d_grads);
-  free(h_state), free(h_f), free(h_p);
+  free(h_state), free(h_f), free(h_f2), free(h_p), free(dense);
   printf("step_driver ok: owner %llu of %llu, %llu chunks\n", (unsigned long long)owner,
          (unsigned long long)R, (unsigned long long)n_chunks);
   return 0;

@@ -1,9 +1,11 @@
 """The C ABI from a plain C program: tests/c_abi/step_driver.c allocates device
-memory with hipMalloc, creates its own stream and runs the fused owner step and
-a checked rank reduce through libzero_shard.so alone (no torch, no Python in
-the process).  Its outputs are checked against the oracle to the same bar as
-the parity tests: reduced gradient and flag bit-exact, master and moments
-within 1e-7 + 1e-6 |x|, 16-bit copy within 1 ulp, squared norm 1e-9 relative.
+memory with hipMalloc, creates its own stream and runs the fused owner step, a
+checked rank reduce (with and without a workspace), the step decision and the
+dense offsets through libzero_shard.so alone (no torch, no Python in the
+process).  Its outputs are checked against the oracle to the same bar as the
+parity tests: reduced gradient and flag bit-exact, master and moments within
+1e-7 + 1e-6 |x|, 16-bit copy within 1 ulp, squared norm 1e-9 relative, the
+clip factor to fp32 rounding of the oracle's, the dense offsets exactly.
 """
 import math
 import os
@@ -69,7 +71,8 @@ def test_c_driver_step_matches_oracle(tmp_path, gcode, pcode, R, owner):
     res = subprocess.run([_driver(), str(inp), str(out)], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, res.stderr
     raw = out.read_bytes()
-    assert len(raw) == 4 * nloc * 4 + 2 * total + 4 + 8
+    tail = 16 * nloc + 2 * total + 4 + 8
+    assert len(raw) == tail + 4 + 4 + 8 + 8 * len(numels)
     fl = np.frombuffer(raw, dtype="<f4", count=3 * nloc)
     gw, gm, gv = fl[:nloc], fl[nloc:2 * nloc], fl[2 * nloc:]
     p16 = np.frombuffer(raw, dtype="<u2", count=total, offset=12 * nloc)
@@ -93,3 +96,12 @@ def test_c_driver_step_matches_oracle(tmp_path, gcode, pcode, R, owner):
     want_flag, want_sumsq = oracle.grad_check(g_or)
     assert flag == want_flag == 0
     assert math.isclose(sumsq, want_sumsq, rel_tol=1e-9)
+    # the decision for this owner alone, and the dense layout
+    update = int(np.frombuffer(raw, dtype="<i4", count=1, offset=tail)[0])
+    coef = float(np.frombuffer(raw, dtype="<f4", count=1, offset=tail + 4)[0])
+    assert update == 1
+    assert coef == pytest.approx(oracle.clip_coef(want_sumsq, 1.0), rel=2 ** -23)
+    dense_total = int(np.frombuffer(raw, dtype="<u8", count=1, offset=tail + 8)[0])
+    dense = np.frombuffer(raw, dtype="<u8", count=len(numels), offset=tail + 16)
+    assert dense_total == sum(numels)
+    assert [int(x) for x in dense] == oracle.dense_offsets(numels)
