@@ -43,7 +43,7 @@ DEFAULT_CHUNK = 2048  # chunk-table granularity (elements) of the timed launches
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=4, choices=(2, 3, 4, 5))
     ap.add_argument("--schedule", default="accumulate", choices=("accumulate", "per-backward"),
