@@ -3,6 +3,7 @@ host calls (layout, chunk table, state accounting, clip scalar, argument
 validation) agree with the oracle.  No device compute runs here.
 """
 import ctypes as ct
+import functools
 import os
 import random
 import re
@@ -414,23 +415,40 @@ def test_noalloc_reduce_rejects_a_check_beyond_its_scratch_before_any_device_cal
     assert "scratch" in L.zero_last_error().decode()
 
 
-def test_device_code_has_no_mixed_precision_fma():
-    """The library's build flags keep the fp16 write-back a rounding of the stored
-    fp32 master weight: without them the compiler folds the fp16 conversion of
-    an fma result into v_fma_mix (one rounding of the exact a*b+c to fp16).
-    The gfx950 assembly of the step kernels, built with those flags, holds no
-    such instruction (and does hold the plain conversions)."""
+@functools.lru_cache(maxsize=None)
+def _device_asm(source: str) -> str:
+    """gfx950 assembly of one of the library's HIP sources, built with its flags."""
     from zero_sharded_optimizer_owned_amd.build import CSRC, HIPCC_FLAGS, INCLUDE
 
     if shutil.which("hipcc") is None:
         pytest.skip("no hipcc")
     flags = [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
     res = subprocess.run(["hipcc", *flags, "-I", INCLUDE, "--cuda-device-only", "-S",
-                          os.path.join(CSRC, "step.hip"), "-o", "-"], capture_output=True, text=True, timeout=300)
+                          os.path.join(CSRC, source), "-o", "-"], capture_output=True, text=True, timeout=300)
     assert res.returncode == 0, res.stderr[-2000:]
-    asm = res.stdout
+    return res.stdout
+
+
+def test_device_code_has_no_mixed_precision_fma():
+    """The library's build flags keep the fp16 write-back a rounding of the stored
+    fp32 master weight: without them the compiler folds the fp16 conversion of
+    an fma result into v_fma_mix (one rounding of the exact a*b+c to fp16).
+    The gfx950 assembly of the step kernels, built with those flags, holds no
+    such instruction (and does hold the plain conversions)."""
+    asm = _device_asm("step.hip")
     assert "v_fma_mix" not in asm and "v_mad_mix" not in asm
     assert "v_cvt_f16_f32" in asm
+
+
+@pytest.mark.parametrize("source", ["step.hip", "copy.hip", "probe.hip"])
+def test_no_kernel_uses_scratch_memory(source):
+    """Every kernel keeps its working set in registers and LDS: the assembler's
+    per-kernel scratch figure is 0 for all of them (a streaming kernel that
+    spills to scratch adds memory traffic of its own)."""
+    asm = _device_asm(source)
+    sizes = [int(x) for x in re.findall(r"; ScratchSize: (\d+)", asm)]
+    assert sizes, "no kernel found"
+    assert max(sizes) == 0, sizes
 
 
 def test_step_decision_is_the_unsharded_clip_and_skip():
