@@ -93,3 +93,37 @@ def test_noalloc_accumulate_modes_equal_the_workspace_form():
             oracle.reduce_add(part, code, D, acc)
         assert_bits_equal(from_dev(out_na)[begin:begin + n], want, f"accumulate {mode} against the oracle")
         del dgr, ws
+
+
+def test_noalloc_at_the_largest_check_its_scratch_array_holds():
+    # the largest n whose check partials fit the 16 MiB array (one element more is
+    # ERANGE, checked on the CPU): accepted, with the same bits, flag and norm as the
+    # workspace form
+    scratch = 16 << 20
+    lo, hi = 1, 1 << 40
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if zs.check_workspace_bytes(mid) <= scratch:
+            lo = mid
+        else:
+            hi = mid
+    n = lo
+    assert zs.check_workspace_bytes(n) <= scratch < zs.check_workspace_bytes(n + 1)
+    print(f"largest checked reduce without a workspace: n={n}", flush=True)
+    g = torch.empty(n, dtype=torch.float16, device=DEV)
+    synth.device_fill(g, synth.stream_key(61, synth.STREAM_GRAD, 0), 0, synth.DIST_NORMAL, 1.0)
+    out_ws = torch.empty(n, dtype=torch.float32, device=DEV)
+    out_na = torch.empty(n, dtype=torch.float32, device=DEV)
+    ov_ws = torch.full((1,), 5, dtype=torch.int32, device=DEV)
+    ss_ws = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+    ov_na = torch.full((1,), 5, dtype=torch.int32, device=DEV)
+    ss_na = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+    ws = zs.check_workspace(n, DEV)
+    zs.zero_reduce_owned([g], 0, n, 1.0, out_ws, check=(ov_ws, ss_ws, ws))
+    zs.zero_reduce_owned_noalloc([g], 0, n, 1.0, out_na, check=(ov_na, ss_na))
+    torch.cuda.synchronize()
+    assert torch.equal(out_na.view(torch.int32), out_ws.view(torch.int32))
+    assert int(ov_na.item()) == int(ov_ws.item()) == 0
+    assert ss_na.item() == ss_ws.item() and ss_ws.item() > 0
+    del g, out_ws, out_na, ws
+    torch.cuda.empty_cache()
