@@ -160,9 +160,9 @@ __device__ __forceinline__ void copy4(const E* s, E* d, uint64_t i, uint64_t n) 
 
 // One span by one block.  When source and destination share their phase
 // within a 16-byte vector, the body moves as 128-bit vectors (consecutive
-// threads on consecutive vectors, up to four per thread in flight) between
-// scalar head and tail pieces; otherwise threads copy single elements.  Spans
-// that do not fit their buffers are skipped.
+// threads on consecutive vectors, up to four per thread and pass of copy4)
+// between scalar head and tail pieces; otherwise threads copy single
+// elements.  Spans that do not fit their buffers are skipped.
 template <typename T>
 __device__ __forceinline__ void span_one(const SpanArgs& a, const zero_copy_span sp, uint64_t t) {
   constexpr uint64_t V = 16 / sizeof(T);
